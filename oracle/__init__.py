@@ -1,0 +1,43 @@
+"""fp64 CPU oracle for exact scaled dot-product attention — TEST INFRASTRUCTURE.
+
+This package is the slow, obviously correct reference that the GPU library is checked
+against.  Only the test suite, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import it; the product path (``online_softmax_attn_amd``) never
+does, and the two share no code.  Everything here is plain NumPy in float64 (mpmath only
+in the tests that pin it).
+
+Sources (the pages' own text; formulas there are partly garbled by HTML extraction):
+  * pierluigilucio.it "Sviluppo AI ed Algebra Lineare", section "Formulazione Algebrica
+    della Self-Attention" — the definition S = QK^T/sqrt(d_k), row softmax, Y = AV.
+  * maeste.it "attention matrix deep" page — the formula softmax(Q K^T / sqrt(d_head)) V,
+    the causal mask (future keys set to -inf before the softmax), decode as a 1 x n row.
+  * el-ai.com "Attenzione: softmax online, riscalamento e memoria" — section 1 (the
+    object computed, max subtraction), section 2 (the (m, l, u) invariant), section 3
+    (worked example), section 4 (merge of disjoint blocks), section 5 (fully masked rows
+    need an explicit convention).
+
+Functions and their pins (tests/test_oracle.py):
+  attention / attend / attention_rows / decode
+      pinned by 50-digit mpmath brute force on tiny inputs, the worked example, row sums,
+      convex hull, shift invariance, closed forms (Q = 0 prefix means, single key,
+      dominant key).
+  online_softmax_scalar / merge / summarize / blocked_softmax
+      pinned by the worked example's step table (and its wrong variant), the block-merge
+      experiment design of el-ai.com section 4, and merge associativity/commutativity.
+No function here is "parity unpinned".
+"""
+
+from .attention import attend, attention, attention_rows, decode, to_f64
+from .online import blocked_softmax, merge, online_softmax_scalar, summarize
+
+__all__ = [
+    "attend",
+    "attention",
+    "attention_rows",
+    "decode",
+    "to_f64",
+    "online_softmax_scalar",
+    "merge",
+    "summarize",
+    "blocked_softmax",
+]

@@ -1,0 +1,150 @@
+"""Materialised fp64 attention: the plain definition, one (batch, head) at a time.
+
+TEST INFRASTRUCTURE (see the package docstring): never imported by the product path.
+
+Definition followed (pierluigilucio.it "Sviluppo AI ed Algebra Lineare", section
+"Formulazione Algebrica della Self-Attention", steps 1-4; maeste.it attention-matrix page,
+the formula and its "softmax" and "V" paragraphs):
+
+    S_ij = scale * <q_i, k_j>                     scale = 1/sqrt(d_head) by default
+    A_ij = exp(S_ij) / sum_{j' valid} exp(S_ij')  over the keys admitted by the mask
+    o_i  = sum_j A_ij v_j
+
+Masks: a causal mask gives query i the keys j <= i (maeste.it: future tokens are set to
+-inf before the softmax); a length mask of n_b admits queries and keys < n_b only.  The
+maximum is subtracted before exponentiating (el-ai.com section 1: it multiplies numerator
+and denominator by the same factor).  A row with no admitted key has no distribution
+(el-ai.com section 5 asks for an explicit convention): its output is 0 and its
+log-sum-exp is -inf.
+
+Everything is materialised — S, the weights, the normaliser — exactly the three-pass
+computation the tiled method avoids; that is what makes it a reference.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def to_f64(x) -> np.ndarray:
+    """Exact upcast of a NumPy array or a CPU/GPU torch tensor (fp32 or bf16) to float64."""
+    if isinstance(x, np.ndarray):
+        return x.astype(np.float64, copy=False)
+    try:  # torch tensor: bf16 -> fp32 is exact, fp32 -> fp64 is exact
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu").to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def attend(S: np.ndarray, V: np.ndarray, valid: np.ndarray | None = None):
+    """Row softmax of scaled scores followed by the weighted sum of values.
+
+    S: [nq, nk] fp64 scores (already scaled).  V: [nk, dv].  valid: bool [nq, nk] or None.
+    Returns (O [nq, dv], lse [nq]) with lse_i = log sum_{j valid} exp(S_ij) (natural log).
+    Rows with no valid key: O = 0, lse = -inf.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    if valid is None:
+        valid = np.ones(S.shape, dtype=bool)
+    has_key = valid.any(axis=1)
+    Sm = np.where(valid, S, -np.inf)
+    m = np.where(has_key, Sm.max(axis=1, initial=-np.inf), 0.0)
+    W = np.where(valid, np.exp(Sm - m[:, None]), 0.0)
+    l = W.sum(axis=1)
+    safe_l = np.where(has_key, l, 1.0)
+    O = (W @ V) / safe_l[:, None]
+    O[~has_key] = 0.0
+    lse = np.where(has_key, m + np.log(safe_l), -np.inf)
+    return O, lse
+
+
+def _valid(nq: int, nk: int, causal: bool, q_offset: int = 0) -> np.ndarray:
+    """Admitted (query, key) pairs; query row r has absolute position q_offset + r."""
+    if not causal:
+        return np.ones((nq, nk), dtype=bool)
+    qi = np.arange(nq)[:, None] + q_offset
+    kj = np.arange(nk)[None, :]
+    return kj <= qi
+
+
+def attention(q, k, v, *, scale: float | None = None, causal: bool = False, seq_lens=None):
+    """Prefill attention over [B, H, n, d] tensors.
+
+    seq_lens: optional length per batch row (host ints); queries and keys at positions
+    >= n_b are padding: their outputs are 0 / lse -inf and they are never read.
+    Returns (O [B, H, n, d] fp64, LSE [B, H, n] fp64).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    B, H, n, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lens = [n] * B if seq_lens is None else [int(x) for x in seq_lens]
+    O = np.zeros((B, H, n, v.shape[-1]))
+    LSE = np.full((B, H, n), -np.inf)
+    for b in range(B):
+        L = lens[b]
+        if L <= 0:
+            continue
+        valid = _valid(L, L, causal)
+        for h in range(H):
+            S = scale * (q[b, h, :L] @ k[b, h, :L].T)
+            O[b, h, :L], LSE[b, h, :L] = attend(S, v[b, h, :L], valid)
+    return O, LSE
+
+
+def attention_rows(q, k, v, rows, *, scale: float | None = None, causal: bool = False, seq_lens=None):
+    """Attention for selected query rows only (the sampled check of long sequences).
+
+    rows: int array [B, H, R] (or [H, R] when B == 1) of query positions.
+    Returns (O [B, H, R, d], LSE [B, H, R]).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    B, H, n, d = q.shape
+    rows = np.asarray(rows)
+    if rows.ndim == 2:
+        rows = rows[None]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lens = [n] * B if seq_lens is None else [int(x) for x in seq_lens]
+    R = rows.shape[-1]
+    O = np.zeros((B, H, R, v.shape[-1]))
+    LSE = np.full((B, H, R), -np.inf)
+    for b in range(B):
+        L = lens[b]
+        for h in range(H):
+            r = rows[b, h]
+            S = scale * (q[b, h, r] @ k[b, h, :L].T)
+            valid = np.ones((R, L), dtype=bool)
+            if causal:
+                valid &= np.arange(L)[None, :] <= r[:, None]
+            valid &= (r < L)[:, None]
+            O[b, h], LSE[b, h] = attend(S, v[b, h, :L], valid)
+    return O, LSE
+
+
+def decode(q, k_seqs, v_seqs, *, scale: float | None = None):
+    """One query per sequence against that sequence's whole cache (no mask inside it).
+
+    q: [B, H, d]; k_seqs / v_seqs: length-B lists of [H, len_b, d] contiguous caches.
+    Returns (O [B, H, d], LSE [B, H]).
+    """
+    q = to_f64(q)
+    B, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, H, d))
+    LSE = np.full((B, H), -np.inf)
+    for b in range(B):
+        kb, vb = to_f64(k_seqs[b]), to_f64(v_seqs[b])
+        for h in range(H):
+            S = scale * (q[b, h][None, :] @ kb[h].T)
+            o, lse = attend(S, vb[h])
+            O[b, h], LSE[b, h] = o[0], lse[0]
+    return O, LSE

@@ -1,0 +1,77 @@
+"""The running (m, l, u) summary of one attention row, in fp64 — TEST INFRASTRUCTURE.
+
+Follows el-ai.com "Attenzione: softmax online, riscalamento e memoria":
+  * section 2: after a prefix of keys keep m (prefix maximum), l (sum of exp(s - m)) and
+    u (the same sum weighted by the values).  For a new pair (s, v) the new maximum is
+    m' = max(m, s); both l AND u are multiplied by exp(m - m') and only then is the new
+    key's exp(s - m') and exp(s - m') * v added.  The first key starts the state at
+    (s_1, 1, v_1), which never forms -inf - (-inf).
+  * section 4: two summaries of disjoint key sets merge the same way: take the larger
+    maximum, bring both normalisers and numerators to it, add.
+The output is o = u / l.  These routines are the algorithm written out step by step in
+plain Python/NumPy; the materialised definition lives in attention.py.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def online_softmax_scalar(scores, values, *, rescale_numerator: bool = True):
+    """Sequential (m, l, u) recurrence over one row.
+
+    scores: sequence of N >= 1 finite floats; values: N vectors.
+    rescale_numerator=False reproduces the flawed variant that rescales only l
+    (el-ai.com section 3 shows it gives a wrong first component).
+    Returns (o, steps) where steps[t] = (m, l, o_t) after t + 1 keys.
+    """
+    scores = [float(s) for s in scores]
+    values = [np.asarray(x, dtype=np.float64) for x in values]
+    if not scores:
+        raise ValueError("a row needs at least one admitted key")
+    if any(not math.isfinite(s) for s in scores):
+        raise ValueError("scores must be finite")
+    m, l, u = scores[0], 1.0, values[0].copy()
+    steps = [(m, l, u / l)]
+    for s, x in zip(scores[1:], values[1:]):
+        m_new = max(m, s)
+        old = math.exp(m - m_new)  # brings every earlier term to the new maximum
+        new = math.exp(s - m_new)
+        l = l * old + new
+        u = (u * old if rescale_numerator else u) + new * x
+        m = m_new
+        steps.append((m, l, u / l))
+    return u / l, steps
+
+
+def summarize(scores, values):
+    """(m, l, u) of one block, computed directly: m = max s, l = sum e^(s-m), u = sum e^(s-m) v."""
+    s = np.asarray(scores, dtype=np.float64)
+    V = np.asarray(values, dtype=np.float64)
+    m = float(s.max())
+    w = np.exp(s - m)
+    return m, float(w.sum()), w @ V
+
+
+def merge(a, b):
+    """Summary of the union of two disjoint key sets (el-ai.com section 4)."""
+    m_a, l_a, u_a = a
+    m_b, l_b, u_b = b
+    m = max(m_a, m_b)
+    f_a = math.exp(m_a - m)
+    f_b = math.exp(m_b - m)
+    return m, l_a * f_a + l_b * f_b, u_a * f_a + u_b * f_b
+
+
+def blocked_softmax(scores, values, block: int):
+    """o for one row computed block by block: summarize each block, fold with merge."""
+    s = np.asarray(scores, dtype=np.float64)
+    V = np.asarray(values, dtype=np.float64)
+    state = None
+    for start in range(0, len(s), block):
+        part = summarize(s[start:start + block], V[start:start + block])
+        state = part if state is None else merge(state, part)
+    m, l, u = state
+    return u / l
