@@ -1,0 +1,232 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one causal bf16 prefill over the [4, 32, 2048, 128] workload (attn_fwd) plus one
+paged decode of 32 sequences x 32 heads, d = 128, KV lengths U{1024..8192} in 16-token
+pages (attn_decode_paged).  Inputs are generated on the host from fixed seeds and moved to
+HBM before timing.  W warm-up steps, then K timed steps bracketed by synchronisations;
+each kernel call is also bracketed by HIP events on the stream it is launched on.
+
+Prints ONE JSON line.  `value` is the prefill throughput in algorithmic TFLOP/s (only the
+admitted causal pairs, QK^T and PV: 4 d B H n(n+1)/2 flops); the decode throughput in
+algorithmic GB/s (the valid K/V tokens, the query, the output and the referenced block
+table entries) is reported beside it.  `roofline` describes the prefill kernel against the
+bf16 dense MFMA peak; `decode.roofline` the decode against HBM.  `cpu_baseline` is the fp64
+oracle timed on this host over a bounded sample of the prefill workload.
+
+--workload long   times the [1, 32, 32768, 128] causal prefill instead (no decode).
+--profile-pass    runs one 1 GiB device copy, one prefill and one decode and exits (the
+                  command the rocprofv3 counter and trace runs wrap).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "online_softmax_attn_amd", "csrc")
+
+
+def kernel_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_FILES = {"prefill": ["fwd_bf16.hip", "common.h"], "decode": ["decode.hip", "common.h"]}
+
+
+def recorded_traffic(kind):
+    """HBM bytes per launch from the committed counter runs, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kind)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_hash") != kernel_hash(KERNEL_FILES[kind]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def causal_flops(B, H, n, d):
+    return 4.0 * d * B * H * n * (n + 1) / 2
+
+
+def decode_bytes(w, H, d):
+    toks = int(w.seq_lens.sum())
+    kv = toks * H * d * 2 * 2
+    qo = 2 * w.q.numel() * 2
+    table = sum(math.ceil(int(L) / w.block_size) for L in w.seq_lens) * 4
+    return kv + qo + table
+
+
+def cpu_baseline(q, k, v, budget_s=12.0):
+    """The oracle as it stands, on (batch, head) pairs of the workload until ~budget_s."""
+    import threadpoolctl
+
+    import oracle
+
+    B, H, n, d = q.shape
+    done, t0 = 0, time.perf_counter()
+    for b in range(B):
+        for h in range(H):
+            oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], causal=True)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    return {
+        "value": causal_flops(1, done, n, d) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {B * H} (batch, head) pairs of the causal prefill "
+                  f"[{B},{H},{n},{d}], fp64 NumPy materialised scores, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["prefill", "long"], default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU sharding is a design, not a build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import online_softmax_attn_amd as attn
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    attn.lib()
+
+    if args.workload == "long":
+        w = workloads.long_prefill()
+        B, H, n, d = w["q"].shape
+        pre_cfg = "causal prefill B=1 H=32 n=32768 d=128 bf16"
+    else:
+        w = workloads.causal_prefill()
+        B, H, n, d = w["q"].shape
+        pre_cfg = "causal prefill B=4 H=32 n=2048 d=128 bf16"
+    q_cpu, k_cpu, v_cpu = w["q"], w["k"], w["v"]
+    q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+    o = torch.empty_like(q)
+    flops = causal_flops(B, H, n, d)
+
+    dec = None
+    if args.workload == "prefill":
+        pw = workloads.paged_decode()
+        dq = pw.q.to(dev)
+        kc, vc = pw.k_cache.to(dev), pw.v_cache.to(dev)
+        tbl, lens = pw.block_table.to(dev), pw.seq_lens.to(dev)
+        do = torch.empty_like(dq)
+        ws = torch.empty(attn.attn_decode_workspace_bytes(32, 32, 128, pw.max_seq_len), dtype=torch.uint8, device=dev)
+        dbytes = decode_bytes(pw, 32, 128)
+        dec = (dq, kc, vc, tbl, lens, do, ws, pw.max_seq_len)
+
+    def prefill():
+        attn.attn_fwd(q, k, v, causal=True, out=o)
+
+    def decode():
+        dq, kc, vc, tbl, lens, do, ws, msl = dec
+        attn.attn_decode_paged(dq, kc, vc, tbl, lens, max_seq_len=msl, out=do, workspace=ws)
+
+    if args.profile_pass:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)            # plain copy of known size: 1 GiB read + 1 GiB written
+        prefill()
+        if dec:
+            decode()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "copy_bytes": 1 << 30, "workload": args.workload}))
+        return
+
+    for _ in range(args.warmup):
+        prefill()
+        if dec:
+            decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        prefill()
+        ev[i][1].record()
+        if dec:
+            decode()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    pre_avg = sum(pre_ms) / K
+    achieved = flops / (pre_avg * 1e-3) / 1e12
+    traffic = recorded_traffic("prefill") if args.workload == "prefill" else None
+    result = {
+        "metric": "attn fwd TFLOPS (causal bf16 prefill) + paged-decode HBM GB/s, % of MI355X peak",
+        "value": round(achieved, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, seeded KV lengths and page permutation)",
+        "config": {"workload": pre_cfg + (" + paged decode B=32 H=32 d=128 lens U[1024,8192] "
+                                          "block 16" if dec else ""),
+                   "batch": B, "heads": H, "seq_len": n, "head_dim": d, "causal": True},
+        "prefill": {"ms_avg": round(pre_avg, 5), "ms_min": round(min(pre_ms), 5),
+                    "tflops": round(achieved, 2), "frac_of_peak": round(achieved / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if dec:
+        dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+        dec_avg = sum(dec_ms) / K
+        gbs = dbytes / (dec_avg * 1e-3) / 1e9
+        result["decode"] = {
+            "value": round(gbs, 1), "unit": "GB/s", "ms_avg": round(dec_avg, 5),
+            "ms_min": round(min(dec_ms), 5), "bytes": dbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic("decode")},
+        }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(q_cpu, k_cpu, v_cpu)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

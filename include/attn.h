@@ -1,0 +1,130 @@
+/*
+ * attn.h — C ABI of the MI355X (gfx950) exact-attention library (libattn.so).
+ *
+ * What the library computes is exact scaled dot-product attention,
+ *     O = softmax(Q K^T * scale) V,     scale normally 1/sqrt(d_head),
+ * as defined on pierluigilucio.it "Sviluppo AI ed Algebra Lineare" (section "Formulazione
+ * Algebrica della Self-Attention") and on the maeste.it attention-matrix page (the formula
+ * softmax(Q K^T / sqrt(d_head)) V and the causal mask).  It is evaluated tile by tile with
+ * the running (m, l, u) summary of el-ai.com "Attenzione: softmax online, riscalamento e
+ * memoria" (section 2: maximum, normaliser and unnormalised accumulator rescaled together),
+ * so the n x n score matrix never exists in device memory; disjoint key ranges are joined
+ * with the merge of its section 4.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers, owned by the caller; the library never
+ *     allocates, frees, synchronises, prints or aborts.  Work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the null stream) and the call returns once it is enqueued.
+ *   - Tensors are dense and row-major with the last dimension fastest.  bf16 is the
+ *     bfloat16 bit pattern (1-8-7), f32 is IEEE binary32.
+ *   - Host-visible arguments are validated before anything is enqueued; on any error
+ *     nothing is enqueued and a status other than ATTN_OK is returned.  Values that live
+ *     in device memory (lengths, block ids) cannot be checked without a synchronisation;
+ *     they are preconditions, stated per function.
+ *   - Unsupported combinations fail loudly with ATTN_ERR_UNSUPPORTED; there is no
+ *     fallback path (the-ai.news fused-kernel page, "Attenzione di tipo FlashAttention e
+ *     attenzione paginata": forcing a backend that cannot take the input must fail).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,     /* null pointer, size <= 0, scale not finite or <= 0, bad block size */
+  ATTN_ERR_UNSUPPORTED = 2, /* dtype / head_dim / option combination this build has no kernel for */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than attn_decode_workspace_bytes() */
+  ATTN_ERR_LAUNCH = 4       /* the HIP runtime refused the launch (hipGetLastError after it) */
+} attn_status;
+
+typedef enum attn_dtype {
+  ATTN_F32 = 0,  /* fp32 in, fp32 out */
+  ATTN_BF16 = 1  /* bf16 in, bf16 out, fp32 accumulation */
+} attn_dtype;
+
+/*
+ * attn_fwd — prefill attention of every query of every (batch, head).
+ *
+ * q, k, v, o : [batch, heads, seq_len, head_dim] of `dtype`, contiguous.  o is written
+ *              in full (padding rows included) and may not alias q, k or v.
+ * lse        : optional (NULL allowed) fp32 [batch, heads, seq_len]; receives the natural
+ *              log of sum_j exp(scale * <q_i, k_j>) over the admitted keys — the saved
+ *              statistic the pages' backward pass recomputes from.
+ * seq_lens   : optional (NULL = every row has seq_len) DEVICE int32 [batch].  Positions
+ *              >= seq_lens[b] are padding: they are never read as keys or values, and their
+ *              query rows get o = 0 and lse = -inf (a row with no admitted key has no
+ *              distribution; this is the explicit convention el-ai.com section 5 asks for).
+ *              Precondition: 1 <= seq_lens[b] <= seq_len.
+ * causal     : nonzero => query i admits keys j <= i only (maeste.it: future keys are set
+ *              to -inf before the softmax).  Combines with seq_lens.
+ * scale      : the factor applied to <q, k>; pass 1/sqrt(head_dim) for the pages' form.
+ * Supported  : ATTN_F32 with head_dim 64 or 128 (scores accumulated in fp64);
+ *              ATTN_BF16 with head_dim 128 (MFMA, fp32 accumulation).
+ */
+attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void* v, void* o,
+                     float* lse, const int32_t* seq_lens, int batch, int heads, int seq_len,
+                     int head_dim, int causal, float scale, void* stream);
+
+/*
+ * attn_decode_workspace_bytes — device bytes attn_decode_paged needs as `workspace` for
+ * these sizes and this split length (kv_split tokens per partial; 0 = the library's
+ * default).  Returns 0 for sizes attn_decode_paged would reject.
+ */
+size_t attn_decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len,
+                                   int kv_split);
+
+/*
+ * attn_decode_paged — one new query per sequence against that sequence's paged K/V cache
+ * (the decode step of the maeste.it page: a 1 x n score row, bound by reading the cache).
+ *
+ * q           : [batch, heads, head_dim] bf16.
+ * k_cache,
+ * v_cache     : [num_blocks, heads, block_size, head_dim] bf16 pools of fixed-size blocks;
+ *               one (block, head) is block_size * head_dim contiguous elements.
+ * block_table : DEVICE int32 [batch, max_blocks_per_seq]; entry i of row b is the pool
+ *               block holding tokens [i*block_size, (i+1)*block_size) of sequence b (the
+ *               block table of the-ai.news page, "attenzione paginata").  Entries past a
+ *               sequence's last block are never read.
+ * seq_lens    : DEVICE int32 [batch]; the query of sequence b admits its tokens
+ *               0 .. seq_lens[b]-1 (no mask inside the cache).  Slots past seq_lens[b] in
+ *               the last block are never used, whatever they hold.
+ *               Preconditions: 1 <= seq_lens[b] <= max_seq_len, every referenced table
+ *               entry in [0, num_blocks).
+ * o           : [batch, heads, head_dim] bf16 output.
+ * lse         : optional fp32 [batch, heads] natural-log normaliser (see attn_fwd).
+ * kv_split    : tokens per split-KV partial, a positive multiple of block_size, or 0 for
+ *               the library's default.  Each (sequence, head, split) produces a partial
+ *               (m, l, u) that a second kernel merges (el-ai.com section 4); the result
+ *               does not depend on kv_split beyond rounding.
+ * workspace   : DEVICE buffer of at least attn_decode_workspace_bytes(batch, heads,
+ *               head_dim, max_seq_len, kv_split) bytes, owned by the caller; its contents on
+ *               entry do not matter.  Concurrent calls must not share one workspace.
+ * Supported   : ATTN_BF16, head_dim 128, block_size 16.
+ */
+attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, void* o, float* lse, int batch,
+                              int heads, int head_dim, int block_size, int num_blocks,
+                              int max_blocks_per_seq, int max_seq_len, float scale,
+                              int kv_split, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* attn_status_str — static, NUL-terminated name of a status code (never NULL). */
+const char* attn_status_str(attn_status status);
+
+/* attn_abi_version — ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,34 @@
+"""Exact scaled dot-product attention for MI355X (gfx950): Python face of libattn.so.
+
+Entry points mirror the C ABI in include/attn.h:
+    attn_fwd                      prefill over [B, H, n, d] (fp32 or bf16), causal/length masks
+    attn_decode_paged             one query per sequence against a paged bf16 K/V cache
+    attn_decode_workspace_bytes   workspace size the decode needs
+    attn_status_str, attn_abi_version
+"""
+
+from .binding import (
+    ATTN_BF16,
+    ATTN_F32,
+    LIB_PATH,
+    AttnError,
+    attn_abi_version,
+    attn_decode_paged,
+    attn_decode_workspace_bytes,
+    attn_fwd,
+    attn_status_str,
+    lib,
+)
+
+__all__ = [
+    "ATTN_BF16",
+    "ATTN_F32",
+    "LIB_PATH",
+    "AttnError",
+    "attn_abi_version",
+    "attn_decode_paged",
+    "attn_decode_workspace_bytes",
+    "attn_fwd",
+    "attn_status_str",
+    "lib",
+]

@@ -1,0 +1,197 @@
+"""Thin ctypes binding of libattn.so (include/attn.h).
+
+The functions carry the C entry points' names.  They only marshal arguments: check
+tensor dtypes, devices, shapes and contiguity, allocate outputs/workspace with torch when
+the caller did not pass them, pass raw device pointers and torch's current HIP stream, and
+raise on a non-OK status.  Every step of the attention itself runs in the HIP kernels; if
+the library is not built this module raises instead of computing anything another way.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_LAUNCH = range(5)
+ATTN_F32, ATTN_BF16 = 0, 1
+
+# name -> (restype, argtypes), exactly the declarations of include/attn.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+SIGNATURES = {
+    "attn_fwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P]),
+    "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "attn_decode_paged": (
+        _I,
+        [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P,
+         ctypes.c_size_t, _P],
+    ),
+    "attn_status_str": (ctypes.c_char_p, [_I]),
+    "attn_abi_version": (_I, []),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func} failed: {attn_status_str(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m online_softmax_attn_amd.build` "
+                "(there is no fallback implementation)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def attn_status_str(status: int) -> str:
+    return lib().attn_status_str(int(status)).decode()
+
+
+def attn_abi_version() -> int:
+    return int(lib().attn_abi_version())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check_dev(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+
+
+_DT = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+
+
+def _lengths(seq_lens, batch, limit, device, name="seq_lens"):
+    """Lengths as a device int32 tensor.
+
+    A host sequence is checked (batch entries, each in [1, limit]) before upload.  A device
+    int32 tensor is passed through unchecked (reading it back would synchronise the
+    stream); its range is then the caller's precondition, as in the C ABI.
+    """
+    if seq_lens is None:
+        return None
+    if isinstance(seq_lens, torch.Tensor) and seq_lens.is_cuda:
+        if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous() or seq_lens.numel() != batch:
+            raise ValueError(f"{name} on the device must be contiguous int32 with {batch} entries")
+        return seq_lens
+    host = torch.as_tensor(seq_lens).to(torch.int64).reshape(-1)
+    if host.numel() != batch:
+        raise ValueError(f"{name} must have {batch} entries")
+    if int(host.min()) < 1 or int(host.max()) > limit:
+        raise ValueError(f"{name} must lie in [1, {limit}]")
+    return host.to(torch.int32).to(device)
+
+
+def attn_fwd(q, k, v, *, causal=False, scale=None, seq_lens=None, out=None, lse=None,
+             return_lse=False, stream=None):
+    """Prefill attention over [B, H, n, d] tensors (fp32 d in {64,128}; bf16 d = 128).
+
+    seq_lens: optional per-batch lengths (host sequence or device int32 tensor); rows past
+    a length are padding (output 0, lse -inf).  Returns o, or (o, lse) with return_lse.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t)
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, n, d] of one shape")
+    B, H, n, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev("out", out, q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must be [B, H, n, d]")
+    if lse is None and return_lse:
+        lse = torch.empty(B, H, n, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if lse.shape != (B, H, n):
+            raise ValueError("lse must be [B, H, n]")
+    lens = _lengths(seq_lens, B, n, q.device)
+    st = lib().attn_fwd(_DT[q.dtype], q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr() if lse is not None else None,
+                        lens.data_ptr() if lens is not None else None,
+                        B, H, n, d, int(bool(causal)), float(scale), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError("attn_fwd", st)
+    return (out, lse) if return_lse else out
+
+
+def attn_decode_workspace_bytes(batch, heads, head_dim, max_seq_len, kv_split=0) -> int:
+    return int(lib().attn_decode_workspace_bytes(batch, heads, head_dim, max_seq_len, kv_split))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, scale=None,
+                      kv_split=0, out=None, lse=None, return_lse=False, workspace=None,
+                      stream=None):
+    """One bf16 query per sequence ([B, H, d]) against a paged cache [blocks, H, 16, d]."""
+    _check_dev("q", q, torch.bfloat16)
+    _check_dev("k_cache", k_cache, torch.bfloat16)
+    _check_dev("v_cache", v_cache, torch.bfloat16)
+    _check_dev("block_table", block_table, torch.int32)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, H, d]; caches [num_blocks, H, block_size, d]")
+    B, H, d = q.shape
+    nb, Hc, bs, dc = k_cache.shape
+    if Hc != H or dc != d:
+        raise ValueError("cache heads / head_dim differ from q")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    if seq_lens is None:
+        raise ValueError("seq_lens is required for decode")
+    lens = _lengths(seq_lens, B, max_seq_len, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev("out", out, torch.bfloat16)
+    if lse is None and return_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+    need = attn_decode_workspace_bytes(B, H, d, max_seq_len, kv_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_dev("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_paged(
+        ATTN_BF16, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        lens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        B, H, d, bs, nb, int(block_table.shape[1]), int(max_seq_len), float(scale),
+        int(kv_split), workspace.data_ptr(), ws_bytes, _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError("attn_decode_paged", st)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,36 @@
+// Shared device types and launch declarations of the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+#define ATTN_LOG2E 1.4426950408889634f
+#define ATTN_LN2 0.6931471805599453f
+
+// Launchers (host side).  Arguments are already validated by the C ABI layer; each returns
+// the HIP status of its launch(es).
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          const int32_t* seq_lens, int batch, int heads, int n, int head_dim,
+                          int causal, float scale, hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* lse,
+                           const int32_t* seq_lens, int batch, int heads, int n, int causal,
+                           float scale, hipStream_t stream);
+
+// Split-KV paged decode: partials into `workspace`, then the merge pass writes o / lse.
+int decode_default_split(int batch, int heads, int max_seq_len);
+size_t decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len, int split);
+hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens, bf16* o,
+                               float* lse, int batch, int heads, int num_blocks,
+                               int max_blocks_per_seq, int max_seq_len, float scale, int split,
+                               void* workspace, hipStream_t stream);

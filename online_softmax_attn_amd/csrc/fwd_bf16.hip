@@ -1,0 +1,272 @@
+// bf16 prefill attention on gfx950 matrix cores, head_dim 128.
+//
+// Method: the score matrix is produced and consumed one 64-key tile at a time with the
+// running (m, l, u) summary of el-ai.com "Attenzione: softmax online, riscalamento e
+// memoria", section 2 (new maximum m' = max(m, rowmax); l and u both multiplied by
+// 2^(m - m'); then the tile's weights and weighted values added), and u is divided by l
+// once at the end (the deferred normalisation pierluigilucio.it "Sviluppo AI ed Algebra
+// Lineare" credits to FlashAttention-2).  Scores never leave registers.
+//
+// Mapping onto CDNA4:
+//   * workgroup = 4 waves = 128 queries of one (batch, head); each wave owns 32 queries.
+//   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the
+//     query is the MFMA column (lane % 32), so a lane holds 32 of one query's 64 tile
+//     scores and the other 32 sit in lane ^ 32.  Row max = in-lane max + one cross-half
+//     exchange; the normaliser stays a per-lane partial until the epilogue.
+//   * the output is accumulated transposed too, O^T += V^T P^T: its column is again the
+//     query, so the rescale factor of a query multiplies that lane's registers only.  The
+//     bf16 weights P^T feed the MFMA B operand straight from the score registers; V^T is
+//     read from a row-major V tile with ds_read_b64_tr_b16, whose 16-lane transpose hands
+//     each lane 4 consecutive keys of one dimension.
+//   * K/V tiles (64 x 128 bf16 = 16 KiB each) are double-buffered in LDS: the next tile is
+//     fetched into registers with 128-bit loads while the current one is consumed, then
+//     stored with an XOR swizzle that keeps both the K row reads and the transposed V
+//     reads free of bank conflicts.  One barrier per tile.
+//   * exp is v_exp_f32 (2^x): scores are scaled by scale*log2(e) inside one FMA.
+//   * the normaliser sums the bf16-ROUNDED weights that enter the P.V product (dot2 with
+//     ones), so rounding of P cancels in u/l to first order.
+//   * causal: tiles strictly above a wave's diagonal are skipped, the grid is issued
+//     heaviest-first, and every query tile of one (batch, head) lands on the same XCD
+//     (workgroups are dealt round-robin to the 8 XCDs) so K/V are re-read from one L2.
+#include "common.h"
+
+namespace {
+
+constexpr int kD = 128;      // head dim
+constexpr int kBM = 128;     // queries per workgroup
+constexpr int kBN = 64;      // keys per tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileElems = kBN * kD;
+
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// LDS element offset of logical 16-byte chunk `c` (0..15) of row `r` in a K tile: the chunk
+// index is XORed with r % 16, so the 16 rows one MFMA operand read touches hit 16 distinct
+// chunk slots.
+__device__ __forceinline__ int k_slot(int r, int c) { return r * kD + ((c ^ (r & 15)) << 3); }
+// Same for a V tile: chunk groups of 64 bytes are XORed with r % 4, so the 8 rows one
+// transposed read touches spread over all four 64-byte bank groups.
+__device__ __forceinline__ int v_slot(int r, int c) { return r * kD + ((c ^ ((r & 3) << 2)) << 3); }
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.f;
+  return z;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ lens, int B,
+    int H, int n, int n_qtiles, int causal, float c_log2) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kTileElems];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kTileElems];
+
+  const int HB = H * B;
+  const int qt = n_qtiles - 1 - (int)(blockIdx.x / HB);  // heaviest causal tiles first
+  const int bh = blockIdx.x % HB;
+  const int b = bh / H;
+  int L = lens ? lens[b] : n;
+  L = L < 0 ? 0 : (L > n ? n : L);
+  const size_t base = (size_t)bh * n * kD;
+  const int m0 = qt * kBM;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int hl = lane >> 5;    // which half of the wave
+  const int lq = lane & 31;    // query column within the wave's 32
+  const int qi = m0 + w * 32 + lq;
+
+  if (m0 >= L) {  // the whole tile is padding: o = 0, lse = -inf
+    for (int i = tid; i < kBM * kD / 8; i += kThreads) {
+      const int r = m0 + (i * 8) / kD;
+      if (r < n) *reinterpret_cast<bf16x8*>(O + base + (size_t)r * kD + (i * 8) % kD) = zero8();
+    }
+    if (LSE)
+      for (int r = m0 + tid; r < min(m0 + kBM, n); r += kThreads) LSE[(size_t)bh * n + r] = -INFINITY;
+    return;
+  }
+
+  // Q^T operand: lane (query lq, half hl) holds dims 16*ks + 8*hl .. +7 for ks = 0..7.
+  bf16x8 qop[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    qop[ks] = (qi < L) ? *reinterpret_cast<const bf16x8*>(Q + base + (size_t)qi * kD + 16 * ks + 8 * hl)
+                       : zero8();
+
+  const int kend = causal ? min(L, m0 + kBM) : L;
+  const int n_tiles = (kend + kBN - 1) / kBN;
+
+  // tile staging: thread handles chunks tid + 256*i (i = 0..3) -> row tid/16 + 16 i, chunk tid%16
+  const int st_row = tid >> 4;
+  const int st_chunk = tid & 15;
+  bf16x8 kst[4], vst[4];
+
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = t * kBN + st_row + 16 * i;
+      if (key < L) {
+        const size_t off = base + (size_t)key * kD + st_chunk * 8;
+        kst[i] = *reinterpret_cast<const bf16x8*>(K + off);
+        vst[i] = *reinterpret_cast<const bf16x8*>(V + off);
+      } else {
+        kst[i] = zero8();
+        vst[i] = zero8();
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = st_row + 16 * i;
+      *reinterpret_cast<bf16x8*>(&Ks[buf][k_slot(r, st_chunk)]) = kst[i];
+      *reinterpret_cast<bf16x8*>(&Vs[buf][v_slot(r, st_chunk)]) = vst[i];
+    }
+  };
+
+  floatx16 acc[4];  // O^T, d blocks of 32: lane holds d = 32*db + 8*(r/4) + 4*hl + r%4
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m_run = -INFINITY;  // running max of scaled scores, log2 units
+  float l_run = 0.f;        // this lane's half of the normaliser
+
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  const int wave_q_first = m0 + w * 32;
+  const int wave_q_last = wave_q_first + 31;
+
+  // transposed-read addressing for V^T (see header): 16-lane group g, source lane s
+  const int g = lane >> 4, s = lane & 15;
+  const int tr_row = 4 * (g >> 1) + (s >> 2);              // + 16*m + 8*read
+  const int tr_col = 16 * (g & 1) + 4 * (s & 3);           // + 32*db
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    const int k0 = t * kBN;
+    const bool skip = causal && (k0 > wave_q_last);
+    if (!skip) {
+      const bf16* Kt = Ks[buf];
+      const bf16* Vt = Vs[buf];
+      // ---- S^T = K Q^T for keys k0 + 32*kb + (0..31)
+      floatx16 sc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+        const int row = 32 * kb + lq;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&Kt[k_slot(row, 2 * ks + hl)]);
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sc[kb], 0, 0, 0);
+        }
+      }
+      // ---- mask: key of (kb, r) is k0 + 32 kb + 8 (r/4) + 4 hl + r%4
+      const bool need_mask = (k0 + kBN > L) || (causal && k0 + kBN - 1 > wave_q_first);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const bool ok = key < L && (!causal || key <= qi);
+            sc[kb][r] = ok ? sc[kb][r] : -INFINITY;
+          }
+      }
+      // ---- online softmax update (log2 units)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * c_log2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+
+      bf16x8 pop[4];  // P^T operand per 16-key group
+      float psum = 0.f;
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int kb = grp >> 1, r0 = 8 * (grp & 1);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          floatx2 pp;
+          pp[0] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + e], c_log2, -m_use));
+          pp[1] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + e + 1], c_log2, -m_use));
+          const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, psum, false);
+          pop[grp][e] = pb[0];
+          pop[grp][e + 1] = pb[1];
+        }
+      }
+      l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int col = 32 * db + tr_col;
+          const int r_lo = 16 * grp + tr_row;
+          const int r_hi = r_lo + 8;
+          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_shortx4*)(&Vt[v_slot(r_lo, col >> 3) + (col & 7)]));
+          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_shortx4*)(&Vt[v_slot(r_hi, col >> 3) + (col & 7)]));
+          const bf16x8 vop = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                                     __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3,
+                                                     4, 5, 6, 7);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[grp], acc[db], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: o = u / l
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qi < n) {
+    bf16* orow = O + base + (size_t)qi * kD;
+    const bool valid = qi < L;
+    const float inv = valid ? 1.0f / l_tot : 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        floatx4 x;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = acc[db][4 * a + c] * inv;
+        const bf16x4 y = __builtin_convertvector(x, bf16x4);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * a + 4 * hl) = y;
+      }
+    if (LSE && hl == 0)
+      LSE[(size_t)bh * n + qi] = valid ? (m_run * ATTN_LN2 + __logf(l_tot)) : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* lse,
+                           const int32_t* seq_lens, int batch, int heads, int n, int causal,
+                           float scale, hipStream_t stream) {
+  const int n_qtiles = (n + kBM - 1) / kBM;
+  const dim3 grid((unsigned)n_qtiles * batch * heads);
+  hipLaunchKernelGGL(fwd_bf16_kernel, grid, dim3(kThreads), 0, stream, q, k, v, o, lse,
+                     seq_lens, batch, heads, n, n_qtiles, causal, scale * ATTN_LOG2E);
+  return hipGetLastError();
+}

@@ -1,0 +1,101 @@
+"""The C ABI: library loads, exports what include/attn.h declares, and rejects bad
+host-visible arguments before touching the GPU (CPU only: every call here fails validation
+and returns before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import online_softmax_attn_amd as attn
+from online_softmax_attn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+FAKE = 0x10000  # a non-null pointer value: validation fails before it could be used
+INVALID, UNSUPPORTED, WORKSPACE = (binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UNSUPPORTED,
+                                   binding.ATTN_ERR_WORKSPACE)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(binding.SIGNATURES), names
+    lib = attn.lib()
+    for name in names:
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_abi_version_matches_header():
+    text = open(HEADER).read()
+    want = int(re.search(r"#define ATTN_ABI_VERSION (\d+)", text).group(1))
+    assert attn.attn_abi_version() == want
+
+
+def test_status_strings():
+    assert attn.attn_status_str(0) == "ATTN_OK"
+    assert attn.attn_status_str(UNSUPPORTED) == "ATTN_ERR_UNSUPPORTED"
+    assert attn.attn_status_str(99) == "ATTN_ERR_UNKNOWN"
+
+
+def fwd(**kw):
+    a = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, lens=None, B=1, H=1, n=16,
+             d=128, causal=0, scale=0.1)
+    a.update(kw)
+    return attn.lib().attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["lens"],
+                               a["B"], a["H"], a["n"], a["d"], a["causal"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(o=None), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(n=0), INVALID),
+    (dict(d=0), INVALID), (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(dtype=0, d=96), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED), (dict(n=1 << 24, d=128), UNSUPPORTED),
+])
+def test_fwd_validation(kw, status):
+    assert fwd(**kw) == status
+
+
+def dec(**kw):
+    a = dict(dtype=1, q=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, lens=FAKE, o=FAKE, lse=None, B=2, H=4,
+             d=128, bs=16, nb=10, mb=8, msl=128, scale=0.1, split=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return attn.lib().attn_decode_paged(a["dtype"], a["q"], a["kc"], a["vc"], a["tbl"], a["lens"],
+                                        a["o"], a["lse"], a["B"], a["H"], a["d"], a["bs"], a["nb"],
+                                        a["mb"], a["msl"], a["scale"], a["split"], a["ws"], a["wsb"],
+                                        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(kc=None), INVALID), (dict(tbl=None), INVALID),
+    (dict(lens=None), INVALID), (dict(o=None), INVALID), (dict(B=0), INVALID),
+    (dict(nb=0), INVALID), (dict(msl=0), INVALID), (dict(scale=0.0), INVALID),
+    (dict(mb=7), INVALID),               # 7 blocks of 16 cannot hold 128 tokens
+    (dict(split=24), INVALID), (dict(split=-16), INVALID), (dict(split=2048), INVALID),
+    (dict(bs=32, mb=4), UNSUPPORTED), (dict(d=64), UNSUPPORTED), (dict(dtype=0), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE),
+])
+def test_decode_validation(kw, status):
+    assert dec(**kw) == status
+
+
+def test_decode_workspace_bytes():
+    f = attn.attn_decode_workspace_bytes
+    # partials: B * H * ceil(max_seq_len / split) entries of (m, l, u[128]) fp32
+    assert f(2, 4, 128, 1000, 256) == 2 * 4 * 4 * 130 * 4
+    assert f(2, 4, 128, 1024, 16) == 2 * 4 * 64 * 130 * 4
+    assert f(2, 4, 128, 1000, 0) > 0
+    assert f(2, 4, 64, 1000, 0) == 0
+    assert f(2, 4, 128, 1000, 24) == 0
+    assert f(0, 4, 128, 1000, 0) == 0
+    need = f(2, 4, 128, 128, 0)
+    assert dec(wsb=need - 1) == WORKSPACE

@@ -1,0 +1,67 @@
+"""Parity of attn_decode_paged with the oracle's decode on the contiguous per-sequence
+caches (the oracle never sees the paged pool, so the block-table translation is checked
+independently), plus poison in unused slots and split-count invariance (merge law)."""
+
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_attn_amd as attn
+import oracle
+import workloads
+from metrics import errs, to64
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN = 1e-2, 1e-3
+
+
+def gpu_decode(w, kv_split=0):
+    q = w.q.cuda()
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), device="cuda")
+    attn.attn_decode_paged(q, w.k_cache.cuda(), w.v_cache.cuda(), w.block_table.cuda(),
+                           w.seq_lens.tolist(), max_seq_len=w.max_seq_len, kv_split=kv_split,
+                           out=out, lse=lse)
+    torch.cuda.synchronize()
+    return to64(out), to64(lse)
+
+
+@pytest.mark.parametrize("lens,split", [([1], 0), ([1, 15, 16, 17], 16), ([33, 250, 256, 257], 32),
+                                        ([1000, 3, 700], 0), ([4096, 1, 2049], 1024),
+                                        ([300, 301], 48)])
+def test_decode_shapes(lens, split):
+    w = workloads.paged(lens, 3, 128, seed=sum(lens), poison=True, spare_blocks=3)
+    print(f"case: decode lens={lens} split={split}", flush=True)
+    o, lse = gpu_decode(w, split)
+    ro, rl = oracle.decode(w.q, w.k_seqs, w.v_seqs)
+    mx, mean = errs(o, ro)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    np.testing.assert_allclose(lse, rl, rtol=2e-6, atol=2e-5)
+    if lens[0] == 1:  # a single cached token returns its value exactly
+        np.testing.assert_array_equal(o[0], to64(w.v_seqs[0][:, 0]))
+
+
+@pytest.mark.parametrize("poison", [False, True])
+def test_decode_workload(poison):
+    w = workloads.paged_decode(poison=poison)
+    print(f"case: paged decode B=32 H=32 poison={poison}", flush=True)
+    o, lse = gpu_decode(w)
+    ro, rl = oracle.decode(w.q, w.k_seqs, w.v_seqs)
+    mx, mean = errs(o, ro)
+    print(f"max-abs {mx:.5f} mean-abs {mean:.2e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    np.testing.assert_allclose(lse, rl, rtol=2e-6, atol=2e-5)
+
+
+def test_decode_split_invariance():
+    """Merging partial (m, l, u) summaries is exact in real arithmetic: any split length
+    gives the same output up to rounding."""
+    w = workloads.paged([5000, 77, 1024, 3333], 4, 128, seed=51)
+    ro, _ = oracle.decode(w.q, w.k_seqs, w.v_seqs)
+    outs = [gpu_decode(w, s)[0] for s in (16, 64, 256, 1024)]
+    for o in outs:
+        mx, mean = errs(o, ro)
+        assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 2 * 2.0 ** -8  # a couple of bf16 ulps at |o| < 1
