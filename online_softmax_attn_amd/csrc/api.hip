@@ -45,8 +45,9 @@ attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void*
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID;
   if (batch <= 0 || heads <= 0 || seq_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID;
   if (!finite_positive(scale)) return ATTN_ERR_INVALID;
-  // 32-bit row indices inside the kernels: bound the element count of one (batch, head)
-  if ((long long)seq_len * head_dim >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  // 32-bit byte offsets inside one (batch, head) slice
+  const long long elem = dtype == ATTN_F32 ? 4 : 2;
+  if ((long long)seq_len * head_dim * elem >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
   if ((long long)batch * heads * ((seq_len + 127) / 128) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ATTN_F32) {

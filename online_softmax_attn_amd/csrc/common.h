@@ -34,3 +34,22 @@ hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v
                                float* lse, int batch, int heads, int num_blocks,
                                int max_blocks_per_seq, int max_seq_len, float scale, int split,
                                void* workspace, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------
+// Buffer resources: loads through a buffer descriptor return 0 for any byte offset at or
+// past `bytes`, which is how out-of-range rows (ragged tails, padding) are zero-filled
+// without branches.  The fourth descriptor word is the gfx9-family default format.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+typedef __attribute__((address_space(3))) void lds_void;
+// 16 bytes per lane from global (buffer offset `voff`) straight into LDS: lane i of the
+// wave writes lds_base + 16 * i.  lds_base must be wave-uniform.
+__device__ __forceinline__ void load_lds16(rsrc_t r, lds_void* lds_base, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 load_b128(rsrc_t r, int voff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}

@@ -38,6 +38,7 @@ constexpr int kBN = 64;      // keys per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileElems = kBN * kD;
+constexpr float kSlack = 8.0f;  // log2 headroom of the lazily raised reference maximum
 
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
@@ -60,8 +61,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ lens, int B,
     int H, int n, int n_qtiles, int causal, float c_log2) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kTileElems];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kTileElems];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][kTileElems];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][kTileElems];
 
   const int HB = H * B;
   const int qt = n_qtiles - 1 - (int)(blockIdx.x / HB);  // heaviest causal tiles first
@@ -89,41 +90,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     return;
   }
 
+  // rows >= L read as zeros through the descriptors' range
+  const uint32_t valid_bytes = (uint32_t)L * kD * 2;
+  const rsrc_t rq = make_rsrc(Q + base, valid_bytes);
+  const rsrc_t rk = make_rsrc(K + base, valid_bytes);
+  const rsrc_t rv = make_rsrc(V + base, valid_bytes);
+
   // Q^T operand: lane (query lq, half hl) holds dims 16*ks + 8*hl .. +7 for ks = 0..7.
   bf16x8 qop[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    qop[ks] = (qi < L) ? *reinterpret_cast<const bf16x8*>(Q + base + (size_t)qi * kD + 16 * ks + 8 * hl)
-                       : zero8();
+  for (int ks = 0; ks < 8; ++ks) qop[ks] = load_b128(rq, (qi * kD + 16 * ks + 8 * hl) * 2);
 
   const int kend = causal ? min(L, m0 + kBM) : L;
   const int n_tiles = (kend + kBN - 1) / kBN;
 
-  // tile staging: thread handles chunks tid + 256*i (i = 0..3) -> row tid/16 + 16 i, chunk tid%16
-  const int st_row = tid >> 4;
-  const int st_chunk = tid & 15;
-  bf16x8 kst[4], vst[4];
-
-  auto load_tile = [&](int t) {
+  // Direct global->LDS tile fill: wave w fills 1 KiB slices 4w..4w+3 of each tile; lane i of
+  // slice j lands in row 4j + i/16, physical chunk i%16, so it fetches the logical chunk the
+  // swizzle puts there.
+  int k_src[4], v_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * (4 * w + i) + (lane >> 4);
+    const int pc = lane & 15;
+    k_src[i] = (r * kD + 8 * (pc ^ (r & 15))) * 2;
+    v_src[i] = (r * kD + 8 * (pc ^ ((r & 3) << 2))) * 2;
+  }
+  auto issue_tile = [&](int t, int buf) {
+    const int toff = t * kBN * kD * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = t * kBN + st_row + 16 * i;
-      if (key < L) {
-        const size_t off = base + (size_t)key * kD + st_chunk * 8;
-        kst[i] = *reinterpret_cast<const bf16x8*>(K + off);
-        vst[i] = *reinterpret_cast<const bf16x8*>(V + off);
-      } else {
-        kst[i] = zero8();
-        vst[i] = zero8();
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = st_row + 16 * i;
-      *reinterpret_cast<bf16x8*>(&Ks[buf][k_slot(r, st_chunk)]) = kst[i];
-      *reinterpret_cast<bf16x8*>(&Vs[buf][v_slot(r, st_chunk)]) = vst[i];
+      const int slice = (4 * w + i) * 512;  // elements
+      load_lds16(rk, (lds_void*)&Ks[buf][slice], toff + k_src[i]);
+      load_lds16(rv, (lds_void*)&Vs[buf][slice], toff + v_src[i]);
     }
   };
 
@@ -132,8 +130,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m_run = -INFINITY;  // running max of scaled scores, log2 units
-  float l_run = 0.f;        // this lane's half of the normaliser
+  // Reference maximum (log2 units) the weights are taken against.  It follows the running
+  // maximum lazily: it is raised (and l, u rescaled by 2^(old - new)) only when some score
+  // of the wave exceeds it by more than kSlack, so weights stay <= 2^kSlack and the
+  // rescale — exact in real arithmetic whichever reference is used — is mostly skipped.
+  float m_ref = -INFINITY;
+  float l_run = 0.f;  // this lane's half of the normaliser
 
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
   const int wave_q_first = m0 + w * 32;
@@ -141,16 +143,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // transposed-read addressing for V^T (see header): 16-lane group g, source lane s
   const int g = lane >> 4, s = lane & 15;
-  const int tr_row = 4 * (g >> 1) + (s >> 2);              // + 16*m + 8*read
+  const int tr_row = 4 * (g >> 1) + (s >> 2);              // + 16*grp + 8*read
   const int tr_col = 16 * (g & 1) + 4 * (s & 3);           // + 32*db
 
-  load_tile(0);
-  store_tile(0);
+  issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1);
     const int k0 = t * kBN;
     const bool skip = causal && (k0 > wave_q_last);
     if (!skip) {
@@ -182,16 +184,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           }
       }
       // ---- online softmax update (log2 units)
-      float mx = -INFINITY;
+      float mx = __builtin_fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[0][r]), sc[0][r + 1]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
+      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[1][r]), sc[1][r + 1]);
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32)) * c_log2;
+      if (__any(mx > m_ref + kSlack)) {
+        // floor at -1e30: a lane with no admitted key yet gets alpha = 0, never NaN
+        const float m_new = __builtin_fmaxf(__builtin_fmaxf(m_ref, mx), -1e30f);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 from the empty state
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      }
+      const float m_use = __builtin_fmaxf(m_ref, -1e30f);  // no -inf - (-inf) on empty rows
 
       bf16x8 pop[4];  // P^T operand per 16-key group
       float psum = 0.f;
@@ -209,11 +219,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           pop[grp][e + 1] = pb[1];
         }
       }
-      l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      l_run += psum;
 
       // ---- O^T += V^T P^T
 #pragma unroll
@@ -234,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
       }
     }
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of tile t+1 has landed in LDS
     __syncthreads();
   }
 
@@ -243,19 +249,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   if (qi < n) {
     bf16* orow = O + base + (size_t)qi * kD;
     const bool valid = qi < L;
-    const float inv = valid ? 1.0f / l_tot : 0.f;
+    const float inv = 1.0f / l_tot;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         floatx4 x;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) x[c] = acc[db][4 * a + c] * inv;
+        for (int c = 0; c < 4; ++c) x[c] = valid ? acc[db][4 * a + c] * inv : 0.f;
         const bf16x4 y = __builtin_convertvector(x, bf16x4);
         *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * a + 4 * hl) = y;
       }
     if (LSE && hl == 0)
-      LSE[(size_t)bh * n + qi] = valid ? (m_run * ATTN_LN2 + __logf(l_tot)) : -INFINITY;
+      LSE[(size_t)bh * n + qi] = valid ? (m_ref * ATTN_LN2 + __logf(l_tot)) : -INFINITY;
   }
 }
 
