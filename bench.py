@@ -16,6 +16,10 @@ oracle timed on this host over a bounded sample of the prefill workload.
 --workload long   times the [1, 32, 32768, 128] causal prefill instead (no decode).
 --profile-pass    runs one 1 GiB device copy, one prefill and one decode and exits (the
                   command the rocprofv3 counter and trace runs wrap).
+--record-traffic FETCH_CSV WRITE_CSV
+                  reads the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE
+                  run of --profile-pass, scales each counter by what it read for the 1 GiB
+                  copy, and writes profiles/traffic.json (bytes per launch + kernel hash).
 """
 
 from __future__ import annotations
@@ -100,7 +104,48 @@ def cpu_baseline(q, k, v, budget_s=12.0):
     }
 
 
+def record_traffic(fetch_csv, write_csv):
+    """profiles/traffic.json from FETCH_SIZE / WRITE_SIZE runs of --profile-pass."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = ("copy" if "copyBuffer" in name else "prefill" if "fwd_bf16_kernel" in name
+                   else "decode_split" if "decode_split_kernel" in name
+                   else "decode_merge" if "decode_merge_kernel" in name else None)
+            if key:
+                vals.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)  # KiB -> B
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = float(1 << 30)
+    f_scale = copy_bytes / max(fetch["copy"])   # the 1 GiB copy reads 1 GiB
+    w_scale = copy_bytes / max(write["copy"])   # and writes 1 GiB
+    out = {"scale": {"FETCH_SIZE": round(f_scale, 4), "WRITE_SIZE": round(w_scale, 4)},
+           "source": "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -- python bench.py --profile-pass"}
+    out["prefill"] = {"kernel_hash": kernel_hash(KERNEL_FILES["prefill"]),
+                      "fetch_bytes": fetch["prefill"][0] * f_scale,
+                      "write_bytes": write["prefill"][0] * w_scale}
+    out["prefill"]["bytes_per_launch"] = out["prefill"]["fetch_bytes"] + out["prefill"]["write_bytes"]
+    dec = {k: fetch[k][0] * f_scale + write[k][0] * w_scale for k in ("decode_split", "decode_merge")}
+    out["decode"] = {"kernel_hash": kernel_hash(KERNEL_FILES["decode"]),
+                     "split_bytes": dec["decode_split"], "merge_bytes": dec["decode_merge"],
+                     "bytes_per_launch": dec["decode_split"] + dec["decode_merge"]}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
+    if len(sys.argv) == 4 and sys.argv[1] == "--record-traffic":
+        record_traffic(sys.argv[2], sys.argv[3])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
