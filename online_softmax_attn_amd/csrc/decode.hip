@@ -12,18 +12,22 @@
 // kernel is shaped for HBM bandwidth — 128-bit loads, the next block's K/V requested before
 // the current one is consumed, the table slice fetched once per split.
 //
-// Lane layout inside a 16 x 128 block (4 KiB for K, 4 KiB for V): lane l owns token l / 4
-// and the four 16-byte chunks (l % 4) + 4 i, i = 0..3, i.e. 32 of the 128 dimensions.  A
-// token's score is a dot2 chain over those 32 dims plus a 4-lane reduction; its weight then
-// scales the same lane's 32 values of V, so the accumulator is per lane and is reduced over
-// the 16 token slots only once, at the end of the split.
+// Lane layout inside a 16 x 128 block (4 KiB for K, 4 KiB for V): one load instruction
+// reads 1 KiB contiguous — lane l takes 16-byte chunk l % 16 (dims 8 (l%16) .. +7) of token
+// 4 i + l / 16 for i = 0..3.  A token's score is a dot2 chain over the lane's 8 dims and a
+// 16-lane DPP reduction; its weight scales the same lane's 8 values of V, so the
+// accumulator is 8 floats per lane, reduced over the four 16-lane groups once per split.
 #include "common.h"
 
 namespace {
 
 constexpr int kD = 128;
 constexpr int kBlock = 16;
-constexpr int kDefaultSplit = 256;
+constexpr int kDefaultSplit = 128;
+#ifndef ATTN_DECODE_DEPTH
+#define ATTN_DECODE_DEPTH 2
+#endif
+constexpr int kDepth = ATTN_DECODE_DEPTH;  // blocks requested ahead of the one being consumed
 
 struct Partials {  // workspace views; index p = (b * H + h) * max_splits + split
   float* m;        // running max, log2 units
@@ -39,6 +43,40 @@ __device__ __forceinline__ Partials partial_views(void* ws, size_t n_part) {
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kCtrl,
+                                                            0xF, 0xF, true));
+}
+// sum over the 16 lanes of a row: swaps within pairs, quads, half-rows, rows
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float xor16(float x) {  // own + lane ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32(float x) {  // own + lane ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+struct Block {
+  uint4 k[4], v[4];  // token 4 i + lane/16, dims 8 (lane%16) .. +7
+};
+
 __global__ __launch_bounds__(64) void decode_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, void* __restrict__ ws,
@@ -50,112 +88,110 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   const int nblk = (L + kBlock - 1) / kBlock;
   const int blk0 = split * split_blocks;
   if (blk0 >= nblk) return;  // beyond this sequence: the merge never reads it
-  const int blk1 = min(blk0 + split_blocks, nblk);
-  const int tok = lane >> 2, qq = lane & 3;
+  const int count = min(blk0 + split_blocks, nblk) - blk0;
+  const int grp = lane >> 4, dc = lane & 15;
 
-  // this lane's 32 query dims as bf16 pairs
-  uint4 qv[4];
-  const bf16* qrow = q + ((size_t)b * H + h) * kD;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) qv[i] = *reinterpret_cast<const uint4*>(qrow + 8 * (qq + 4 * i));
-
+  // this lane's 8 query dims as bf16 pairs
+  const uint4 qv = *reinterpret_cast<const uint4*>(q + ((size_t)b * H + h) * kD + 8 * dc);
   // table slice for this split: lane j holds entry blk0 + j
-  const int tbl = (lane < blk1 - blk0) ? table[(size_t)b * max_blocks_per_seq + blk0 + lane] : 0;
+  const int tbl = (lane < count) ? table[(size_t)b * max_blocks_per_seq + blk0 + lane] : 0;
 
-  float m_run = -INFINITY, l_run = 0.f;
-  float acc[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-
-  const size_t head_off = (size_t)h * kBlock * kD + (size_t)tok * kD;
   const size_t blk_stride = (size_t)H * kBlock * kD;
-
-  uint4 kb[4], vb[4], kn[4], vn[4];
-  auto fetch = [&](int j, uint4* kd, uint4* vd) {
+  const size_t lane_off = (size_t)h * kBlock * kD + (size_t)grp * kD + 8 * dc;
+  auto fetch = [&](int j, Block& d) {
     // out-of-contract block ids are clamped into the pool rather than read out of bounds
     const int phys = min(max(__builtin_amdgcn_readlane(tbl, j), 0), num_blocks - 1);
-    const bf16* kp = kc + (size_t)phys * blk_stride + head_off;
-    const bf16* vp = vc + (size_t)phys * blk_stride + head_off;
+    const bf16* kp = kc + (size_t)phys * blk_stride + lane_off;
+    const bf16* vp = vc + (size_t)phys * blk_stride + lane_off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d.k[i] = *reinterpret_cast<const uint4*>(kp + 4 * i * kD);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d.v[i] = *reinterpret_cast<const uint4*>(vp + 4 * i * kD);
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+
+  auto consume = [&](int j, const Block& d) {
+    float s[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      kd[i] = *reinterpret_cast<const uint4*>(kp + 8 * (qq + 4 * i));
-      vd[i] = *reinterpret_cast<const uint4*>(vp + 8 * (qq + 4 * i));
+      const uint32_t* kw = reinterpret_cast<const uint32_t*>(&d.k[i]);
+      const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qv);
+      float x = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw[e]),
+                                            __builtin_bit_cast(bf16x2, qw[e]), x, false);
+      s[i] = row_sum16(x);
+    }
+    const int tok0 = (blk0 + j) * kBlock + grp;  // token of s[i] is tok0 + 4 i
+    const bool tail = (blk0 + j + 1) * kBlock > L;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = (!tail || tok0 + 4 * i < L) ? s[i] * c_log2 : -INFINITY;
+      mx = __builtin_fmaxf(mx, s[i]);
+    }
+    mx = max32(max16(mx));
+    // every block holds at least one admitted token, so mx and m_new are finite
+    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
+    l_run = fmaf(l_run, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // a slot past the sequence end never enters the sum, whatever it holds
+      if (tail && tok0 + 4 * i >= L) continue;
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(&d.v[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(p[i], bf_lo(vw[e]), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(p[i], bf_hi(vw[e]), acc[2 * e + 1]);
+      }
     }
   };
 
-  fetch(0, kb, vb);
-  for (int j = 0; j < blk1 - blk0; ++j) {
-    if (j + 1 < blk1 - blk0) fetch(j + 1, kn, vn);
-    // score of this lane's token
-    float s = 0.f;
+  // software pipeline: kDepth + 1 register buffers, loads kDepth blocks ahead
+  Block buf[kDepth + 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kb[i]);
-      const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qv[i]);
+  for (int j = 0; j < kDepth; ++j)
+    if (j < count) fetch(j, buf[j]);
+  int j = 0;
+  for (; j + kDepth + 1 <= count; j += kDepth + 1) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw[e]),
-                                            __builtin_bit_cast(bf16x2, qw[e]), s, false);
-    }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    const int key = (blk0 + j) * kBlock + tok;
-    const bool ok = key < L;
-    s = ok ? s * c_log2 : -INFINITY;
-    float mx = s;
-    mx = fmaxf(mx, __shfl_xor(mx, 4));
-    mx = fmaxf(mx, __shfl_xor(mx, 8));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // every block holds at least one admitted token, so mx and m_new are finite
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float p = __builtin_amdgcn_exp2f(s - m_new);
-    m_run = m_new;
-    l_run = fmaf(l_run, alpha, p);
-    if (ok) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vb[i]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[8 * i + 2 * e] = fmaf(p, bf_lo(vw[e]), acc[8 * i + 2 * e] * alpha);
-          acc[8 * i + 2 * e + 1] = fmaf(p, bf_hi(vw[e]), acc[8 * i + 2 * e + 1] * alpha);
-        }
-      }
-    } else {  // slot past the sequence end: its value is never read (it may be anything)
-#pragma unroll
-      for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kb[i] = kn[i];
-      vb[i] = vn[i];
+    for (int r = 0; r <= kDepth; ++r) {
+      if (j + r + kDepth < count) fetch(j + r + kDepth, buf[(r + kDepth) % (kDepth + 1)]);
+      consume(j + r, buf[r]);
     }
   }
+#pragma unroll
+  for (int r = 0; r <= kDepth; ++r)
+    if (j + r < count) consume(j + r, buf[r]);
 
-  // reduce over the 16 token slots (lanes with equal lane % 4)
+  // reduce over the four 16-lane groups (each lane summed its own tokens)
+  l_run = xor32(xor16(l_run));
 #pragma unroll
-  for (int off = 4; off < 64; off <<= 1) {
-    l_run += __shfl_xor(l_run, off);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] += __shfl_xor(acc[i], off);
-  }
+  for (int c = 0; c < 8; ++c) acc[c] = xor32(xor16(acc[c]));
   const Partials P = partial_views(ws, n_part);
   const size_t p = ((size_t)b * H + h) * max_splits + split;
-  if (lane < 4) {
-    float* u = P.u + p * kD;
+  if (lane < 16) {
+    float* u = P.u + p * kD + 8 * dc;
+    floatx4 lo, hi;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      floatx4 lo, hi;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        lo[c] = acc[8 * i + c];
-        hi[c] = acc[8 * i + 4 + c];
-      }
-      *reinterpret_cast<floatx4*>(u + 8 * (lane + 4 * i)) = lo;
-      *reinterpret_cast<floatx4*>(u + 8 * (lane + 4 * i) + 4) = hi;
+    for (int c = 0; c < 4; ++c) {
+      lo[c] = acc[c];
+      hi[c] = acc[4 + c];
     }
+    *reinterpret_cast<floatx4*>(u) = lo;
+    *reinterpret_cast<floatx4*>(u + 4) = hi;
     if (lane == 0) {
       P.m[p] = m_run;
       P.l[p] = l_run;
@@ -163,32 +199,43 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   }
 }
 
-// merge of the partial summaries of one (sequence, head); thread = one dimension
-__global__ __launch_bounds__(kD) void decode_merge_kernel(
+// merge of the partial summaries of one (sequence, head): one wave, lane = 2 dimensions
+__global__ __launch_bounds__(64) void decode_merge_kernel(
     const void* __restrict__ ws, const int32_t* __restrict__ lens, bf16* __restrict__ o,
     float* __restrict__ lse, int H, int max_seq_len, int max_splits, int split_tokens,
     size_t n_part) {
   const int h = blockIdx.x, b = blockIdx.y;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x;
   const int L = min(max(lens[b], 0), max_seq_len);
   const int ns = (L + split_tokens - 1) / split_tokens;
+  const size_t out = ((size_t)b * H + h) * kD + 2 * lane;
   if (ns == 0) {  // no admitted key (out of contract): the empty-row convention
-    o[((size_t)b * H + h) * kD + d] = (bf16)0.f;
-    if (lse && d == 0) lse[(size_t)b * H + h] = -INFINITY;
+    o[out] = (bf16)0.f;
+    o[out + 1] = (bf16)0.f;
+    if (lse && lane == 0) lse[(size_t)b * H + h] = -INFINITY;
     return;
   }
   const Partials P = partial_views(const_cast<void*>(ws), n_part);
   const size_t p0 = ((size_t)b * H + h) * max_splits;
   float mstar = -INFINITY;
-  for (int s = 0; s < ns; ++s) mstar = fmaxf(mstar, P.m[p0 + s]);
-  float lsum = 0.f, usum = 0.f;
+  for (int s = lane; s < ns; s += 64) mstar = __builtin_fmaxf(mstar, P.m[p0 + s]);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) mstar = __builtin_fmaxf(mstar, __shfl_xor(mstar, off));
+  float lsum = 0.f, u0 = 0.f, u1 = 0.f;
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) {
     const float w = __builtin_amdgcn_exp2f(P.m[p0 + s] - mstar);
+    const floatx2 uu = *reinterpret_cast<const floatx2*>(P.u + (p0 + s) * kD + 2 * lane);
     lsum = fmaf(w, P.l[p0 + s], lsum);
-    usum = fmaf(w, P.u[(p0 + s) * kD + d], usum);
+    u0 = fmaf(w, uu[0], u0);
+    u1 = fmaf(w, uu[1], u1);
   }
-  o[((size_t)b * H + h) * kD + d] = (bf16)(usum / lsum);
-  if (lse && d == 0) lse[(size_t)b * H + h] = mstar * ATTN_LN2 + __logf(lsum);
+  const float inv = 1.0f / lsum;
+  floatx2 r;
+  r[0] = u0 * inv;
+  r[1] = u1 * inv;
+  *reinterpret_cast<bf16x2*>(o + out) = __builtin_convertvector(r, bf16x2);
+  if (lse && lane == 0) lse[(size_t)b * H + h] = mstar * ATTN_LN2 + __logf(lsum);
 }
 
 }  // namespace
@@ -219,7 +266,7 @@ hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v
                      scale * ATTN_LOG2E, n_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(heads, batch), dim3(kD), 0, stream, workspace,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(heads, batch), dim3(64), 0, stream, workspace,
                      seq_lens, o, lse, heads, max_seq_len, max_splits, split, n_part);
   return hipGetLastError();
 }

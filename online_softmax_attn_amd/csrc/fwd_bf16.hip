@@ -57,6 +57,23 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
+// value of lane l ^ 32 (v_permlane32_swap exchanges the two wave halves)
+__device__ __forceinline__ float other_half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float other_half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+
+struct Tile {
+  floatx16 s[2];  // S^T of 64 keys: lane holds key 32 kb + 8 (r/4) + 4 hl + r%4 of query lq
+};
+
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ lens, int B,
@@ -103,6 +120,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   const int kend = causal ? min(L, m0 + kBM) : L;
   const int n_tiles = (kend + kBN - 1) / kBN;
+  const int wave_q_first = m0 + w * 32;
+  const int wave_q_last = wave_q_first + 31;
+  // tiles a wave takes part in (causal: none strictly above its diagonal)
+  const int wave_tiles = causal ? min(n_tiles, wave_q_last / kBN + 1) : n_tiles;
 
   // Direct global->LDS tile fill: wave w fills 1 KiB slices 4w..4w+3 of each tile; lane i of
   // slice j lands in row 4j + i/16, physical chunk i%16, so it fetches the logical chunk the
@@ -115,14 +136,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     k_src[i] = (r * kD + 8 * (pc ^ (r & 15))) * 2;
     v_src[i] = (r * kD + 8 * (pc ^ ((r & 3) << 2))) * 2;
   }
-  auto issue_tile = [&](int t, int buf) {
-    const int toff = t * kBN * kD * 2;
+  auto issue_k = [&](int t, int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slice = (4 * w + i) * 512;  // elements
-      load_lds16(rk, (lds_void*)&Ks[buf][slice], toff + k_src[i]);
-      load_lds16(rv, (lds_void*)&Vs[buf][slice], toff + v_src[i]);
-    }
+    for (int i = 0; i < 4; ++i)
+      load_lds16(rk, (lds_void*)&Ks[buf][(4 * w + i) * 512], t * kBN * kD * 2 + k_src[i]);
+  };
+  auto issue_v = [&](int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      load_lds16(rv, (lds_void*)&Vs[buf][(4 * w + i) * 512], t * kBN * kD * 2 + v_src[i]);
   };
 
   floatx16 acc[4];  // O^T, d blocks of 32: lane holds d = 32*db + 8*(r/4) + 4*hl + r%4
@@ -135,117 +157,168 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // of the wave exceeds it by more than kSlack, so weights stay <= 2^kSlack and the
   // rescale — exact in real arithmetic whichever reference is used — is mostly skipped.
   float m_ref = -INFINITY;
-  float l_run = 0.f;  // this lane's half of the normaliser
+  float m_use = -1e30f;  // m_ref floored: no -inf - (-inf) on rows with no key yet
+  float l_run = 0.f;     // this lane's half of the normaliser
 
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  const int wave_q_first = m0 + w * 32;
-  const int wave_q_last = wave_q_first + 31;
 
   // transposed-read addressing for V^T (see header): 16-lane group g, source lane s
   const int g = lane >> 4, s = lane & 15;
   const int tr_row = 4 * (g >> 1) + (s >> 2);              // + 16*grp + 8*read
   const int tr_col = 16 * (g & 1) + 4 * (s & 3);           // + 32*db
 
-  issue_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1);
-    const int k0 = t * kBN;
-    const bool skip = causal && (k0 > wave_q_last);
-    if (!skip) {
-      const bf16* Kt = Ks[buf];
-      const bf16* Vt = Vs[buf];
-      // ---- S^T = K Q^T for keys k0 + 32*kb + (0..31)
-      floatx16 sc[2];
+  // ---- building blocks ----------------------------------------------------------------
+  auto compute_s = [&](Tile& T, const bf16* Kt) {  // S^T = K Q^T, 16 MFMA + 16 LDS reads
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) T.s[kb][r] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
-        const int row = 32 * kb + lq;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&Kt[k_slot(row, 2 * ks + hl)]);
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sc[kb], 0, 0, 0);
-        }
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&Kt[k_slot(32 * kb + lq, 2 * ks + hl)]);
+        T.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], T.s[kb], 0, 0, 0);
       }
-      // ---- mask: key of (kb, r) is k0 + 32 kb + 8 (r/4) + 4 hl + r%4
-      const bool need_mask = (k0 + kBN > L) || (causal && k0 + kBN - 1 > wave_q_first);
-      if (need_mask) {
+  };
+  auto apply_mask = [&](Tile& T, int k0) {  // key of (kb, r) is k0 + 32 kb + 8 (r/4) + 4 hl + r%4
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool ok = key < L && (!causal || key <= qi);
-            sc[kb][r] = ok ? sc[kb][r] : -INFINITY;
-          }
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool ok = key < L && (!causal || key <= qi);
+        T.s[kb][r] = ok ? T.s[kb][r] : -INFINITY;
       }
-      // ---- online softmax update (log2 units)
-      float mx = __builtin_fmaxf(sc[0][0], sc[0][1]);
+  };
+  auto need_mask = [&](int t) {
+    const int k0 = t * kBN;
+    return (k0 + kBN > L) || (causal && k0 + kBN - 1 > wave_q_first);
+  };
+  auto row_max = [&](const Tile& T) {  // scaled (log2 units) max over this tile's 64 keys
+    float mx = __builtin_fmaxf(T.s[0][0], T.s[0][1]);
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[0][r]), sc[0][r + 1]);
+    for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, T.s[0][r]), T.s[0][r + 1]);
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[1][r]), sc[1][r + 1]);
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32)) * c_log2;
-      if (__any(mx > m_ref + kSlack)) {
-        // floor at -1e30: a lane with no admitted key yet gets alpha = 0, never NaN
-        const float m_new = __builtin_fmaxf(__builtin_fmaxf(m_ref, mx), -1e30f);
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 from the empty state
-        m_ref = m_new;
-        l_run *= alpha;
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, T.s[1][r]), T.s[1][r + 1]);
+    return other_half_max(mx) * c_log2;
+  };
+  auto raise_ref = [&](float mx) {  // the lazy rescale of l and u
+    if (__any(mx > m_ref + kSlack)) {
+      // floor at -1e30: a lane with no admitted key yet gets alpha = 0, never NaN
+      const float m_new = __builtin_fmaxf(__builtin_fmaxf(m_ref, mx), -1e30f);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 from the empty state
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      }
-      const float m_use = __builtin_fmaxf(m_ref, -1e30f);  // no -inf - (-inf) on empty rows
-
-      bf16x8 pop[4];  // P^T operand per 16-key group
-      float psum = 0.f;
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    m_use = __builtin_fmaxf(m_ref, -1e30f);
+  };
+  auto weights = [&](const Tile& T, bf16x8 (&pop)[4]) {  // P^T operand, returns its row sum
+    float psum = 0.f;
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int kb = grp >> 1, r0 = 8 * (grp & 1);
+    for (int grp = 0; grp < 4; ++grp) {
+      const int kb = grp >> 1, r0 = 8 * (grp & 1);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          floatx2 pp;
-          pp[0] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + e], c_log2, -m_use));
-          pp[1] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + e + 1], c_log2, -m_use));
-          const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-          psum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, psum, false);
-          pop[grp][e] = pb[0];
-          pop[grp][e + 1] = pb[1];
-        }
-      }
-      l_run += psum;
-
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int col = 32 * db + tr_col;
-          const int r_lo = 16 * grp + tr_row;
-          const int r_hi = r_lo + 8;
-          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_shortx4*)(&Vt[v_slot(r_lo, col >> 3) + (col & 7)]));
-          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_shortx4*)(&Vt[v_slot(r_hi, col >> 3) + (col & 7)]));
-          const bf16x8 vop = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
-                                                     __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3,
-                                                     4, 5, 6, 7);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[grp], acc[db], 0, 0, 0);
-        }
+      for (int e = 0; e < 8; e += 2) {
+        floatx2 pp;
+        pp[0] = __builtin_amdgcn_exp2f(fmaf(T.s[kb][r0 + e], c_log2, -m_use));
+        pp[1] = __builtin_amdgcn_exp2f(fmaf(T.s[kb][r0 + e + 1], c_log2, -m_use));
+        const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, psum, false);
+        pop[grp][e] = pb[0];
+        pop[grp][e + 1] = pb[1];
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of tile t+1 has landed in LDS
+    return psum;
+  };
+  auto pv = [&](const bf16* Vt, const bf16x8 (&pop)[4]) {  // O^T += V^T P^T
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int col = 32 * db + tr_col;
+        const int r_lo = 16 * grp + tr_row;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_shortx4*)(&Vt[v_slot(r_lo, col >> 3) + (col & 7)]));
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_shortx4*)(&Vt[v_slot(r_lo + 8, col >> 3) + (col & 7)]));
+        const bf16x8 vop = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                                   __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3,
+                                                   4, 5, 6, 7);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[grp], acc[db], 0, 0, 0);
+      }
+  };
+
+  // One pipelined step: the weights of tile t (in `cur`) are formed while the matrix cores
+  // compute the scores of tile t+1 (into `nxt`); then P(t) V(t) is accumulated while the
+  // row maximum of tile t+1 is taken.  Loads run two tiles ahead for K, one for V.
+  auto step = [&](int t, Tile& cur, Tile& nxt) {
+    const bool has_next = t + 1 < n_tiles;
+    if (t + 2 < n_tiles) issue_k(t + 2, t & 1);
+    if (has_next) issue_v(t + 1, (t + 1) & 1);
+    if (t < wave_tiles) {
+      const bool do_next = t + 1 < wave_tiles;
+      bf16x8 pop[4];
+      float psum;
+      if (do_next) {
+        compute_s(nxt, Ks[(t + 1) & 1]);
+        psum = weights(cur, pop);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 6, 0);
+          if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        }
+      } else {
+        psum = weights(cur, pop);
+      }
+      l_run += psum;
+      if (do_next && need_mask(t + 1)) apply_mask(nxt, (t + 1) * kBN);
+      float mx = 0.f;
+      if (do_next) {
+        pv(Vs[t & 1], pop);
+        mx = row_max(nxt);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 1, 1);
+          if (i < 14) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 1);
+        }
+        raise_ref(mx);
+      } else {
+        pv(Vs[t & 1], pop);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the next tiles has landed
     __syncthreads();
+  };
+
+  // ---- prologue: K(0), V(0), K(1) in flight; scores and max of tile 0
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (n_tiles > 1) issue_k(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  Tile ta, tb;
+  compute_s(ta, Ks[0]);
+  if (need_mask(0)) apply_mask(ta, 0);
+  raise_ref(row_max(ta));
+  __syncthreads();  // every wave is done with K(0) before K(2) overwrites its buffer
+
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, ta, tb);
+    if (t + 1 < n_tiles) step(t + 1, tb, ta);
   }
 
   // ---- epilogue: o = u / l
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = other_half_sum(l_run);
   if (qi < n) {
     bf16* orow = O + base + (size_t)qi * kD;
     const bool valid = qi < L;
