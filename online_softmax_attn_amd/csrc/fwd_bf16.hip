@@ -284,12 +284,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       if (do_next) {
         pv(Vs[t & 1], pop);
         mx = row_max(nxt);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 8, 1);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 1);
           __builtin_amdgcn_sched_group_barrier(kSchedVALU, 1, 1);
-          if (i < 14) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 1);
+          if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 1);
         }
         raise_ref(mx);
       } else {
