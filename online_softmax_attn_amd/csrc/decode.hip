@@ -20,10 +20,16 @@
 #include "common.h"
 
 namespace {
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// K/V are read exactly once: non-temporal loads keep them from displacing useful cache
+// lines (measured: +6% bandwidth on the decode workload).
+__device__ __forceinline__ uint4 load_stream(const bf16* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
 
 constexpr int kD = 128;
 constexpr int kBlock = 16;
-constexpr int kDefaultSplit = 128;
 #ifndef ATTN_DECODE_DEPTH
 #define ATTN_DECODE_DEPTH 2
 #endif
@@ -82,7 +88,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, void* __restrict__ ws,
     int H, int num_blocks, int max_blocks_per_seq, int max_seq_len, int max_splits,
     int split_blocks, float c_log2, size_t n_part) {
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // heads fastest: waves dispatched together read neighbouring 4 KiB pieces of one block
+  const int h = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int L = min(max(lens[b], 0), max_seq_len);  // out-of-contract lengths stay in bounds
   const int nblk = (L + kBlock - 1) / kBlock;
@@ -104,9 +111,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const bf16* kp = kc + (size_t)phys * blk_stride + lane_off;
     const bf16* vp = vc + (size_t)phys * blk_stride + lane_off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d.k[i] = *reinterpret_cast<const uint4*>(kp + 4 * i * kD);
+    for (int i = 0; i < 4; ++i) d.k[i] = load_stream(kp + 4 * i * kD);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d.v[i] = *reinterpret_cast<const uint4*>(vp + 4 * i * kD);
+    for (int i = 0; i < 4; ++i) d.v[i] = load_stream(vp + 4 * i * kD);
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -240,11 +247,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 
 }  // namespace
 
+// Split length: as long as possible (each split wave streams its blocks back to back) while
+// the grid still offers enough waves to keep every CU's memory pipeline full.  Measured on
+// the decode workload (B=32, H=32, lengths up to 8192): 128 tokens 407 us, 256: 390 us,
+// 512: 376 us, 768: 376 us, 1024: 378 us.
 int decode_default_split(int batch, int heads, int max_seq_len) {
-  (void)batch;
-  (void)heads;
-  (void)max_seq_len;
-  return kDefaultSplit;
+  constexpr long long kTargetWaves = 8192;
+  for (int split : {512, 256, 128}) {
+    const long long waves = (long long)batch * heads * ((max_seq_len + split - 1) / split);
+    if (waves >= kTargetWaves) return split;
+  }
+  return 64;
 }
 
 size_t decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len, int split) {
@@ -260,7 +273,7 @@ hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v
                                void* workspace, hipStream_t stream) {
   const int max_splits = (max_seq_len + split - 1) / split;
   const size_t n_part = (size_t)batch * heads * max_splits;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(max_splits, heads, batch), dim3(64), 0, stream,
+  hipLaunchKernelGGL(decode_split_kernel, dim3(heads, max_splits, batch), dim3(64), 0, stream,
                      q, k_cache, v_cache, block_table, seq_lens, workspace, heads, num_blocks,
                      max_blocks_per_seq, max_seq_len, max_splits, split / kBlock,
                      scale * ATTN_LOG2E, n_part);
