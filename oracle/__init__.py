@@ -24,10 +24,15 @@ Functions and their pins (tests/test_oracle.py):
   online_softmax_scalar / merge / summarize / blocked_softmax
       pinned by the worked example's step table (and its wrong variant), the block-merge
       experiment design of el-ai.com section 4, and merge associativity/commutativity.
+  attention_grad (backward.py)
+      pinned by 50-digit central differences of the forward definition (masks, padding)
+      and by closed forms (sum of dK is zero; sum of dV is the sum of dO; Q = 0 gives
+      dK = 0; single-key rows send no gradient to q or k).
 No function here is "parity unpinned".
 """
 
 from .attention import attend, attention, attention_rows, decode, to_f64
+from .backward import attention_grad
 from .online import blocked_softmax, merge, online_softmax_scalar, summarize
 
 __all__ = [
@@ -36,6 +41,7 @@ __all__ = [
     "attention_rows",
     "decode",
     "to_f64",
+    "attention_grad",
     "online_softmax_scalar",
     "merge",
     "summarize",

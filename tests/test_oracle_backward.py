@@ -1,0 +1,95 @@
+"""Pins of the oracle's attention gradients (CPU only): the derivative's definition at 50
+digits, and closed forms that follow from the invariances of the forward pass."""
+
+import math
+
+import mpmath
+import numpy as np
+import pytest
+
+import oracle
+
+mpmath.mp.dps = 50
+
+
+def _mp_loss(q, k, v, dout, scale, causal, L):
+    """sum(O * dout) by the forward definition at 50 digits (rows >= L are padding)."""
+    n, d, dv = len(q), len(q[0]), len(v[0])
+    total = mpmath.mpf(0)
+    for i in range(min(n, L)):
+        keys = [j for j in range(L) if (not causal or j <= i)]
+        w = [mpmath.exp(scale * mpmath.fsum(q[i][c] * k[j][c] for c in range(d))) for j in keys]
+        den = mpmath.fsum(w)
+        for c in range(dv):
+            o = mpmath.fsum(wj * v[j][c] for wj, j in zip(w, keys)) / den
+            total += o * dout[i][c]
+    return total
+
+
+def _mp_grad(x, f, h=mpmath.mpf("1e-15")):
+    g = np.zeros((len(x), len(x[0])))
+    for i in range(len(x)):
+        for c in range(len(x[0])):
+            old = x[i][c]
+            x[i][c] = old + h
+            up = f()
+            x[i][c] = old - h
+            dn = f()
+            x[i][c] = old
+            g[i, c] = float((up - dn) / (2 * h))
+    return g
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_gradients_against_50_digit_finite_differences(case):
+    rng = np.random.default_rng(300 + case)
+    n = [1, 2, 3, 4, 5, 3, 4, 5][case]
+    d = [1, 2, 3, 2, 3, 1, 3, 2][case]
+    causal = bool(case % 2)
+    L = n if case < 6 else n - 2
+    spread = [1.0, 3.0, 8.0][case % 3]
+    q, k, v, do = (rng.normal(size=(n, d)) * s for s in (spread, spread, 1.0, 1.0))
+    scale = 1 / math.sqrt(d)
+    dq, dk, dv = oracle.attention_grad(q[None, None], k[None, None], v[None, None], do[None, None],
+                                       causal=causal, seq_lens=[L])
+    mq = [[mpmath.mpf(float(x)) for x in row] for row in q]
+    mk = [[mpmath.mpf(float(x)) for x in row] for row in k]
+    mv = [[mpmath.mpf(float(x)) for x in row] for row in v]
+    mdo = [[mpmath.mpf(float(x)) for x in row] for row in do]
+    msc = mpmath.mpf(scale)
+
+    def f():
+        return _mp_loss(mq, mk, mv, mdo, msc, causal, L)
+
+    for got, x in ((dq, mq), (dk, mk), (dv, mv)):
+        want = _mp_grad(x, f)
+        np.testing.assert_allclose(got[0, 0], want, rtol=1e-12, atol=1e-13)
+
+
+def test_key_sum_and_value_sum_closed_forms():
+    """K + 1 w^T leaves every output unchanged, so sum_j dK_j = 0; V + 1 c^T shifts every
+    valid output by c, so sum_j dV_j = sum over valid rows of dO_i."""
+    rng = np.random.default_rng(310)
+    B, H, n, d = 2, 2, 24, 6
+    q, k, v, do = (rng.normal(size=(B, H, n, d)) for _ in range(4))
+    for causal in (False, True):
+        lens = [n, 13]
+        dq, dk, dv = oracle.attention_grad(q, k, v, do, causal=causal, seq_lens=lens)
+        np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+        for b, L in enumerate(lens):
+            np.testing.assert_allclose(dv[b].sum(axis=1), do[b, :, :L].sum(axis=1), atol=1e-12)
+            assert np.all(dq[b, :, L:] == 0) and np.all(dk[b, :, L:] == 0) and np.all(dv[b, :, L:] == 0)
+
+
+def test_zero_queries_give_zero_key_gradient_and_single_key_rows():
+    rng = np.random.default_rng(311)
+    q = np.zeros((1, 1, 9, 4))
+    k, v, do = (rng.normal(size=(1, 1, 9, 4)) for _ in range(3))
+    dq, dk, dv = oracle.attention_grad(q, k, v, do, causal=True)
+    assert np.all(dk == 0)
+    # row 0 sees only key 0: its weight is identically 1, so it sends no gradient to q_0
+    np.testing.assert_allclose(dq[0, 0, 0], 0.0, atol=1e-15)
+    # a length-1 sequence: dV_0 = dO_0, no gradient to q or k
+    dq1, dk1, dv1 = oracle.attention_grad(q + 1.0, k, v, do, seq_lens=[1])
+    np.testing.assert_array_equal(dv1[0, 0, 0], do[0, 0, 0])
+    assert np.all(dq1 == 0) and np.all(dk1 == 0)
