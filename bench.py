@@ -14,6 +14,10 @@ bf16 dense MFMA peak; `decode.roofline` the decode against HBM.  `cpu_baseline` 
 oracle timed on this host over a bounded sample of the prefill workload.
 
 --workload long   times the [1, 32, 32768, 128] causal prefill instead (no decode).
+--workload backward
+                  times attn_bwd on the [4, 32, 2048, 128] causal workload (dO ~ N(0,1)),
+                  in algorithmic TFLOP/s: the five products QK^T, dO V^T, P^T dO, dS K,
+                  dS^T Q over the admitted pairs, 2.5x the forward's count.
 --profile-pass    runs one 1 GiB device copy, one prefill and one decode and exits (the
                   command the rocprofv3 counter and trace runs wrap).
 --record-traffic FETCH_CSV WRITE_CSV
@@ -142,6 +146,51 @@ def record_traffic(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
+def bench_backward(args):
+    import torch
+
+    import online_softmax_attn_amd as attn
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.causal_prefill()
+    B, H, n, d = w["q"].shape
+    g = torch.Generator().manual_seed(33)
+    q, k, v = w["q"].to(dev), w["k"].to(dev), w["v"].to(dev)
+    do = torch.randn(B, H, n, d, generator=g).to(torch.bfloat16).to(dev)
+    o, lse = attn.attn_fwd(q, k, v, causal=True, return_lse=True)
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(attn.attn_bwd_workspace_bytes(B, H, n), dtype=torch.uint8, device=dev)
+
+    def step():
+        attn.attn_bwd(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        step()
+        e[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    flops = 2.5 * causal_flops(B, H, n, d)
+    tf = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "attn bwd TFLOPS (causal bf16, recomputation from the saved lse)",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO)",
+        "config": {"workload": "causal backward B=4 H=32 n=2048 d=128 bf16 -> fp32 grads"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "ms_avg": round(ms, 5)}))
+
+
 def main():
     if len(sys.argv) == 4 and sys.argv[1] == "--record-traffic":
         record_traffic(sys.argv[2], sys.argv[3])
@@ -150,7 +199,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["prefill", "long"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "long", "backward"], default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     args = ap.parse_args()
@@ -170,6 +219,8 @@ def main():
     torch.cuda.set_device(dev)
     attn.lib()
 
+    if args.workload == "backward":
+        return bench_backward(args)
     if args.workload == "long":
         w = workloads.long_prefill()
         B, H, n, d = w["q"].shape

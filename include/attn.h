@@ -41,7 +41,7 @@ typedef enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_INVALID = 1,     /* null pointer, size <= 0, scale not finite or <= 0, bad block size */
   ATTN_ERR_UNSUPPORTED = 2, /* dtype / head_dim / option combination this build has no kernel for */
-  ATTN_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than attn_decode_workspace_bytes() */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace null or smaller than the matching *_workspace_bytes() */
   ATTN_ERR_LAUNCH = 4       /* the HIP runtime refused the launch (hipGetLastError after it) */
 } attn_status;
 
@@ -72,6 +72,33 @@ typedef enum attn_dtype {
 attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void* v, void* o,
                      float* lse, const int32_t* seq_lens, int batch, int heads, int seq_len,
                      int head_dim, int causal, float scale, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes — device bytes attn_bwd needs as `workspace` (one fp32 per query
+ * row: D_i = <dO_i, O_i>).  Returns 0 for sizes attn_bwd would reject.
+ */
+size_t attn_bwd_workspace_bytes(int batch, int heads, int seq_len);
+
+/*
+ * attn_bwd — gradients of L = sum(O * dO) with respect to q, k and v, by recomputation: the
+ * backward pass of pierluigilucio.it "Sviluppo AI ed Algebra Lineare" (section "Ricalcolo
+ * nel Backward Pass"), which keeps only the forward's per-row normalisation statistics and
+ * recomputes the weight blocks P_ij = exp(scale <q_i, k_j> - lse_i) from q, k, v.
+ *
+ * q, k, v, o, dout : [batch, heads, seq_len, head_dim] of `dtype`, contiguous; o and lse
+ *              are the outputs attn_fwd produced for these q, k, v, mask and scale.
+ * lse        : fp32 [batch, heads, seq_len] (required).
+ * seq_lens, causal, scale : as in attn_fwd (same values as the forward call).
+ * dq, dk, dv : fp32 [batch, heads, seq_len, head_dim], written in full (padding rows 0).
+ * workspace  : DEVICE buffer of at least attn_bwd_workspace_bytes() bytes, owned by the
+ *              caller; contents on entry do not matter.
+ * Supported  : ATTN_BF16 with head_dim 128.
+ */
+attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse,
+                     const int32_t* seq_lens, float* dq, float* dk, float* dv, int batch,
+                     int heads, int seq_len, int head_dim, int causal, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_decode_workspace_bytes — device bytes attn_decode_paged needs as `workspace` for

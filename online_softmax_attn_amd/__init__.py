@@ -2,6 +2,8 @@
 
 Entry points mirror the C ABI in include/attn.h:
     attn_fwd                      prefill over [B, H, n, d] (fp32 or bf16), causal/length masks
+    attn_bwd                      gradients dq, dk, dv by recomputation from the saved lse
+    attn_bwd_workspace_bytes      workspace size the backward pass needs
     attn_decode_paged             one query per sequence against a paged bf16 K/V cache
     attn_decode_workspace_bytes   workspace size the decode needs
     attn_status_str, attn_abi_version
@@ -13,6 +15,8 @@ from .binding import (
     LIB_PATH,
     AttnError,
     attn_abi_version,
+    attn_bwd,
+    attn_bwd_workspace_bytes,
     attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_fwd,
@@ -26,6 +30,8 @@ __all__ = [
     "LIB_PATH",
     "AttnError",
     "attn_abi_version",
+    "attn_bwd",
+    "attn_bwd_workspace_bytes",
     "attn_decode_paged",
     "attn_decode_workspace_bytes",
     "attn_fwd",

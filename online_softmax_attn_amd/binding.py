@@ -26,6 +26,12 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 SIGNATURES = {
     "attn_fwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P]),
+    "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "attn_bwd": (
+        _I,
+        [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P,
+         ctypes.c_size_t, _P],
+    ),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "attn_decode_paged": (
         _I,
@@ -148,6 +154,52 @@ def attn_fwd(q, k, v, *, causal=False, scale=None, seq_lens=None, out=None, lse=
     if st != ATTN_OK:
         raise AttnError("attn_fwd", st)
     return (out, lse) if return_lse else out
+
+
+def attn_bwd_workspace_bytes(batch, heads, seq_len) -> int:
+    return int(lib().attn_bwd_workspace_bytes(batch, heads, seq_len))
+
+
+def attn_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, seq_lens=None, dq=None,
+             dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) in fp32 of sum(o * dout), recomputing the weights from lse.
+
+    q, k, v, o, dout: bf16 [B, H, n, 128]; lse: fp32 [B, H, n] from attn_fwd(return_lse=True)
+    with the same mask, lengths and scale.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_dev(name, t, torch.bfloat16)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, n, d]")
+    B, H, n, d = q.shape
+    _check_dev("lse", lse, torch.float32)
+    if lse.shape != (B, H, n):
+        raise ValueError("lse must be [B, H, n]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        _check_dev(name, t, torch.float32)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must be [B, H, n, d]")
+        outs.append(t)
+    need = attn_bwd_workspace_bytes(B, H, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_dev("workspace", workspace)
+    lens = _lengths(seq_lens, B, n, q.device)
+    st = lib().attn_bwd(ATTN_BF16, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        dout.data_ptr(), lse.data_ptr(), lens.data_ptr() if lens is not None else None,
+                        outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), B, H, n, d,
+                        int(bool(causal)), float(scale), workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError("attn_bwd", st)
+    return tuple(outs)
 
 
 def attn_decode_workspace_bytes(batch, heads, head_dim, max_seq_len, kv_split=0) -> int:

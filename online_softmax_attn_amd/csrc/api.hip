@@ -67,6 +67,31 @@ attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void*
   return ATTN_ERR_UNSUPPORTED;
 }
 
+size_t attn_bwd_workspace_bytes(int batch, int heads, int seq_len) {
+  if (batch <= 0 || heads <= 0 || seq_len <= 0) return 0;
+  return bwd_workspace_bytes(batch, heads, seq_len);
+}
+
+attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse,
+                     const int32_t* seq_lens, float* dq, float* dk, float* dv, int batch,
+                     int heads, int seq_len, int head_dim, int causal, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_INVALID;
+  if (batch <= 0 || heads <= 0 || seq_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID;
+  if (!finite_positive(scale)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  // 32-bit byte offsets inside one (batch, head) slice; one fp32 gradient row is 512 bytes
+  if ((long long)seq_len * head_dim * 4 >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)batch * heads * ((seq_len + 127) / 128) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < bwd_workspace_bytes(batch, heads, seq_len))
+    return ATTN_ERR_WORKSPACE;
+  return launch_status(launch_bwd_bf16(
+      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+      static_cast<const bf16*>(o), static_cast<const bf16*>(dout), lse, seq_lens, dq, dk, dv,
+      batch, heads, seq_len, causal != 0, scale, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t attn_decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len,
                                    int kv_split) {
   if (batch <= 0 || heads <= 0 || head_dim != 128 || max_seq_len <= 0) return 0;

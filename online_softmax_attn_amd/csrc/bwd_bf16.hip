@@ -1,0 +1,430 @@
+// Backward pass of exact attention on gfx950 matrix cores: bf16 inputs, head_dim 128, fp32
+// gradients.
+//
+// pierluigilucio.it "Sviluppo AI ed Algebra Lineare" (section "Ricalcolo nel Backward Pass")
+// describes it: the forward pass keeps only the per-row normalisation statistics, and the
+// backward pass recomputes the score and probability blocks from Q, K and V instead of
+// reading an n x n matrix.  Here the statistic is the log-sum-exp L_i the forward writes,
+// so a recomputed weight is P_ij = exp(scale <q_i, k_j> - L_i).  With D_i = <dO_i, O_i>
+// (= sum_j P_ij dP_ij):
+//     dV_j = sum_i P_ij dO_i            dP_ij = <dO_i, v_j>
+//     dS_ij = P_ij (dP_ij - D_i)        dQ_i = scale sum_j dS_ij k_j
+//                                       dK_j = scale sum_i dS_ij q_i
+// Three kernels: D (a row reduction), dQ (one wave per 32 queries, sweeping key tiles, as
+// the forward pass does) and dK/dV (one wave per 32 keys, sweeping query tiles).  Both
+// sweeps use the forward's register layouts: the MFMA column is the row that owns the
+// accumulator (a query for dQ, a key for dK/dV), weights go from the score registers to
+// the B operand as bf16, and the transposed A operands (K^T for dQ; dO^T and Q^T for dK/dV)
+// come from row-major LDS tiles through ds_read_b64_tr_b16.  Masked pairs get weight 0 by
+// selection, so padding never enters a sum whatever it holds.
+#include "common.h"
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kThreads = 256;
+constexpr int kTile = 64;  // rows per streamed LDS tile
+constexpr int kTileElems = kTile * kD;
+
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// LDS tile swizzle (16-byte chunks of 256-byte rows) that serves both access kinds: the
+// 16 consecutive rows of one 16-byte operand read land in 16 distinct chunk slots, and the
+// 8 rows of one transposed read spread over all four 64-byte bank groups.
+__device__ __forceinline__ int sw_slot(int r, int c) {
+  return r * kD + ((c ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 3);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int n) {
+  const int L = lens ? lens[b] : n;
+  return L < 0 ? 0 : (L > n ? n : L);
+}
+
+// Fill a 64-row bf16 tile (rows t*64 .. t*64+63 of the descriptor's range) straight into
+// LDS: wave w writes 1 KiB slices 4w..4w+3; lane i of slice j lands in row 4j + i/16, chunk
+// slot i%16, and fetches the logical chunk the swizzle puts there.
+struct TileFill {
+  int src[4];
+  __device__ TileFill(int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * (4 * w + i) + (lane >> 4);
+      const int pc = lane & 15;
+      const int c = pc ^ (((r & 3) << 2) | ((r >> 2) & 3));
+      src[i] = (r * kD + 8 * c) * 2;
+    }
+  }
+  __device__ void issue(rsrc_t rs, bf16* dst, int t, int w) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      load_lds16(rs, (lds_void*)&dst[(4 * w + i) * 512], t * kTile * kD * 2 + src[i]);
+  }
+};
+
+// The transposed operand of one 16-row group of a tile: lane (column l % 32, half h) gets
+// rows 16 g + 8 (e/4) + 4 h + e%4 (e = 0..7) of column 32 db + l % 32.
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int g, int db, int lane) {
+  const int tg = lane >> 4, ts = lane & 15;
+  const int col = 32 * db + 16 * (tg & 1) + 4 * (ts & 3);
+  const int r_lo = 16 * g + 4 * (tg >> 1) + (ts >> 2);
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(&tile[sw_slot(r_lo, col >> 3) + (col & 7)]));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(&tile[sw_slot(r_lo + 8, col >> 3) + (col & 7)]));
+  return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ------------------------------------------------------------------------ D = <dO_i, O_i>
+__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restrict__ O,
+                                                           const bf16* __restrict__ dO,
+                                                           float* __restrict__ Dv,
+                                                           const int32_t* __restrict__ lens,
+                                                           int H, int n, long long rows) {
+  const long long row = ((long long)blockIdx.x * kThreads + threadIdx.x) >> 4;  // 16 lanes per row
+  const int part = threadIdx.x & 15;
+  const bool live = row < rows;
+  float x = 0.f;
+  if (live) {
+    const uint4 o = *reinterpret_cast<const uint4*>(O + row * kD + 8 * part);
+    const uint4 g = *reinterpret_cast<const uint4*>(dO + row * kD + 8 * part);
+    const uint32_t* ow = reinterpret_cast<const uint32_t*>(&o);
+    const uint32_t* gw = reinterpret_cast<const uint32_t*>(&g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ow[e]), __builtin_bit_cast(bf16x2, gw[e]), x, false);
+  }
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  if (live && part == 0) {
+    const long long bh = row / n;
+    const int i = (int)(row % n);
+    const int L = clamp_len(lens, (int)(bh / H), n);
+    Dv[row] = i < L ? x : 0.f;
+  }
+}
+
+// ------------------------------------------------------------------------ dQ
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    const int32_t* __restrict__ lens, float* __restrict__ dQ, int B, int H, int n,
+    int n_qtiles, int causal, float c_log2, float scale) {
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][kTileElems];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][kTileElems];
+  constexpr int kBM = 128;
+
+  const int HB = H * B;
+  const int qt = n_qtiles - 1 - (int)(blockIdx.x / HB);  // heaviest causal tiles first
+  const int bh = blockIdx.x % HB;
+  const int L = clamp_len(lens, bh / H, n);
+  const size_t base = (size_t)bh * n * kD;
+  const int m0 = qt * kBM;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hl = lane >> 5, lq = lane & 31;
+  const int qi = m0 + 32 * w + lq;
+
+  if (m0 >= L) {
+    for (int i = tid; i < kBM * kD / 4; i += kThreads) {
+      const int r = m0 + (i * 4) / kD;
+      if (r < n) *reinterpret_cast<floatx4*>(dQ + base + (size_t)r * kD + (i * 4) % kD) = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+
+  const uint32_t valid_bytes = (uint32_t)L * kD * 2;
+  const rsrc_t rq = make_rsrc(Q + base, valid_bytes);
+  const rsrc_t rk = make_rsrc(K + base, valid_bytes);
+  const rsrc_t rv = make_rsrc(V + base, valid_bytes);
+  const rsrc_t rg = make_rsrc(dO + base, valid_bytes);
+
+  bf16x8 qop[8], gop[8];  // Q^T and dO^T operands: dims 16 ks + 8 hl .. +7 of query qi
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qop[ks] = load_b128(rq, (qi * kD + 16 * ks + 8 * hl) * 2);
+    gop[ks] = load_b128(rg, (qi * kD + 16 * ks + 8 * hl) * 2);
+  }
+  const bool row_ok = qi < L;
+  const float lse2 = row_ok ? LSE[(size_t)bh * n + qi] * ATTN_LOG2E : 0.f;
+  const float Di = row_ok ? Dv[(size_t)bh * n + qi] : 0.f;
+
+  const int kend = causal ? min(L, m0 + kBM) : L;
+  const int n_tiles = (kend + kTile - 1) / kTile;
+  const int wave_q_first = m0 + 32 * w, wave_q_last = wave_q_first + 31;
+  const int wave_tiles = causal ? min(n_tiles, wave_q_last / kTile + 1) : n_tiles;
+  const TileFill fill(w, lane);
+
+  floatx16 acc[4];  // dQ^T: lane holds d = 32 db + 8 (r/4) + 4 hl + r%4 of query qi
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  fill.issue(rk, Ks[0], 0, w);
+  fill.issue(rv, Vs[0], 0, w);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) {
+      fill.issue(rk, Ks[buf ^ 1], t + 1, w);
+      fill.issue(rv, Vs[buf ^ 1], t + 1, w);
+    }
+    if (t < wave_tiles) {
+      const bf16* Kt = Ks[buf];
+      const bf16* Vt = Vs[buf];
+      const int k0 = t * kTile;
+      floatx16 s[2], dp[2];  // S^T and dP^T: lane holds key 32 kb + 8 (r/4) + 4 hl + r%4
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[kb][r] = 0.f;
+          dp[kb][r] = 0.f;
+        }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kt[sw_slot(32 * kb + lq, 2 * ks + hl)]);
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vt[sw_slot(32 * kb + lq, 2 * ks + hl)]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[ks], s[kb], 0, 0, 0);
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gop[ks], dp[kb], 0, 0, 0);
+        }
+      const bool need_mask = !row_ok || (k0 + kTile > L) || (causal && k0 + kTile - 1 > wave_q_first);
+      bf16x8 dsop[4];
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int kb = grp >> 1, r0 = 8 * (grp & 1);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          floatx2 d2;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = r0 + e + u;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -lse2));
+            if (need_mask) {
+              const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+              const bool ok = row_ok && key < L && (!causal || key <= qi);
+              p = ok ? p : 0.f;
+            }
+            d2[u] = p * (dp[kb][r] - Di);
+          }
+          const bf16x2 db2 = __builtin_convertvector(d2, bf16x2);
+          dsop[grp][e] = db2[0];
+          dsop[grp][e + 1] = db2[1];
+        }
+      }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Kt, grp, db, lane), dsop[grp], acc[db], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (qi < n) {
+    float* drow = dQ + base + (size_t)qi * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        floatx4 x;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = row_ok ? acc[db][4 * a + c] * scale : 0.f;
+        *reinterpret_cast<floatx4*>(drow + 32 * db + 8 * a + 4 * hl) = x;
+      }
+  }
+}
+
+// ------------------------------------------------------------------------ dK, dV
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    const int32_t* __restrict__ lens, float* __restrict__ dK, float* __restrict__ dV, int B,
+    int H, int n, int causal, float c_log2, float scale) {
+  __shared__ __attribute__((aligned(1024))) bf16 Qs[2][kTileElems];
+  __shared__ __attribute__((aligned(1024))) bf16 Gs[2][kTileElems];
+  __shared__ __attribute__((aligned(16))) float Ls[2][kTile];  // log2-unit LSE; +inf on padding
+  __shared__ __attribute__((aligned(16))) float Ds[2][kTile];
+  constexpr int kBK = 128;
+
+  const int HB = H * B;
+  const int kt = (int)(blockIdx.x / HB);  // key block 0 has the most causal work: first
+  const int bh = blockIdx.x % HB;
+  const int L = clamp_len(lens, bh / H, n);
+  const size_t base = (size_t)bh * n * kD;
+  const int k0 = kt * kBK;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hl = lane >> 5, lq = lane & 31;
+  const int kj = k0 + 32 * w + lq;  // this lane's key
+
+  if (k0 >= L) {
+    for (int i = tid; i < kBK * kD / 4; i += kThreads) {
+      const int r = k0 + (i * 4) / kD;
+      if (r < n) {
+        *reinterpret_cast<floatx4*>(dK + base + (size_t)r * kD + (i * 4) % kD) = floatx4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<floatx4*>(dV + base + (size_t)r * kD + (i * 4) % kD) = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return;
+  }
+
+  const uint32_t valid_bytes = (uint32_t)L * kD * 2;
+  const rsrc_t rq = make_rsrc(Q + base, valid_bytes);
+  const rsrc_t rk = make_rsrc(K + base, valid_bytes);
+  const rsrc_t rv = make_rsrc(V + base, valid_bytes);
+  const rsrc_t rg = make_rsrc(dO + base, valid_bytes);
+
+  bf16x8 kop[8], vop[8];  // K^T and V^T operands of this lane's key
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    kop[ks] = load_b128(rk, (kj * kD + 16 * ks + 8 * hl) * 2);
+    vop[ks] = load_b128(rv, (kj * kD + 16 * ks + 8 * hl) * 2);
+  }
+  const bool key_ok = kj < L;
+  const int wave_k_first = k0 + 32 * w, wave_k_last = wave_k_first + 31;
+
+  const int t0 = causal ? k0 / kTile : 0;  // first query tile that admits any key here
+  const int t1 = (L + kTile - 1) / kTile;
+  const TileFill fill(w, lane);
+  auto issue = [&](int t, int buf) {
+    fill.issue(rq, Qs[buf], t, w);
+    fill.issue(rg, Gs[buf], t, w);
+    if (tid < kTile) {
+      const int q = t * kTile + tid;
+      Ls[buf][tid] = q < L ? LSE[(size_t)bh * n + q] * ATTN_LOG2E : INFINITY;
+      Ds[buf][tid] = q < L ? Dv[(size_t)bh * n + q] : 0.f;
+    }
+  };
+
+  floatx16 ak[4], av[4];  // dK^T, dV^T: lane holds d = 32 db + 8 (r/4) + 4 hl + r%4 of key kj
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ak[db][r] = 0.f;
+      av[db][r] = 0.f;
+    }
+
+  issue(t0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
+    if (t + 1 < t1) issue(t + 1, buf ^ 1);
+    const bf16* Qt = Qs[buf];
+    const bf16* Gt = Gs[buf];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int q0 = t * kTile + 32 * qb;
+      if (causal && q0 + 31 < wave_k_first) continue;  // every query of the block precedes every key
+      floatx16 s, dp;  // S and dP: lane holds query q0 + 8 (r/4) + 4 hl + r%4 of key kj
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qt[sw_slot(32 * qb + lq, 2 * ks + hl)]);
+        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gt[sw_slot(32 * qb + lq, 2 * ks + hl)]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[ks], dp, 0, 0, 0);
+      }
+      const bool need_mask = !key_ok || (k0 + kBK > L) || (causal && q0 < wave_k_last);
+      bf16x8 pop[2], dsop[2];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const floatx4 l4 = *reinterpret_cast<const floatx4*>(&Ls[buf][32 * qb + 8 * a + 4 * hl]);
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds[buf][32 * qb + 8 * a + 4 * hl]);
+        floatx4 p4, ds4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * a + c;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l4[c]));  // 0 on padding rows
+          if (need_mask) {
+            const int q = q0 + 8 * a + 4 * hl + c;
+            const bool ok = key_ok && (!causal || kj <= q);
+            p = ok ? p : 0.f;
+          }
+          p4[c] = p;
+          ds4[c] = p * (dp[r] - d4[c]);
+        }
+        const bf16x4 pb = __builtin_convertvector(p4, bf16x4);
+        const bf16x4 db4 = __builtin_convertvector(ds4, bf16x4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {  // register 4a + c is element 4 (a%2) + c of group a/2
+          pop[a >> 1][4 * (a & 1) + c] = pb[c];
+          dsop[a >> 1][4 * (a & 1) + c] = db4[c];
+        }
+      }
+      // dV^T += dO^T P ; dK^T += Q^T dS
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          av[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Gt, 2 * qb + g, db, lane), pop[g], av[db], 0, 0, 0);
+          ak[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Qt, 2 * qb + g, db, lane), dsop[g], ak[db], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (kj < n) {
+    float* krow = dK + base + (size_t)kj * kD;
+    float* vrow = dV + base + (size_t)kj * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        floatx4 xk, xv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          xk[c] = key_ok ? ak[db][4 * a + c] * scale : 0.f;
+          xv[c] = key_ok ? av[db][4 * a + c] : 0.f;
+        }
+        *reinterpret_cast<floatx4*>(krow + 32 * db + 8 * a + 4 * hl) = xk;
+        *reinterpret_cast<floatx4*>(vrow + 32 * db + 8 * a + 4 * hl) = xv;
+      }
+  }
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int batch, int heads, int n) {
+  return (size_t)batch * heads * n * sizeof(float);
+}
+
+hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
+                           const bf16* dout, const float* lse, const int32_t* seq_lens,
+                           float* dq, float* dk, float* dv, int batch, int heads, int n,
+                           int causal, float scale, void* workspace, hipStream_t stream) {
+  float* Dv = static_cast<float*>(workspace);
+  const long long rows = (long long)batch * heads * n;
+  const unsigned pre_blocks = (unsigned)((rows * 16 + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3(pre_blocks), dim3(kThreads), 0, stream, o, dout, Dv,
+                     seq_lens, heads, n, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const float c_log2 = scale * ATTN_LOG2E;
+  const int n_qtiles = (n + 127) / 128;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)n_qtiles * batch * heads), dim3(kThreads), 0,
+                     stream, q, k, v, dout, lse, Dv, seq_lens, dq, batch, heads, n, n_qtiles,
+                     causal, c_log2, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_ktiles = (n + 127) / 128;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)n_ktiles * batch * heads), dim3(kThreads), 0,
+                     stream, q, k, v, dout, lse, Dv, seq_lens, dk, dv, batch, heads, n, causal,
+                     c_log2, scale);
+  return hipGetLastError();
+}

@@ -26,6 +26,14 @@ hipError_t launch_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* o,
                            const int32_t* seq_lens, int batch, int heads, int n, int causal,
                            float scale, hipStream_t stream);
 
+// Backward pass (bf16 in, fp32 gradients): D = rowsum(dO * O) into `workspace`, then dQ
+// and dK/dV kernels that recompute the weights from the saved log-sum-exp.
+size_t bwd_workspace_bytes(int batch, int heads, int n);
+hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
+                           const bf16* dout, const float* lse, const int32_t* seq_lens,
+                           float* dq, float* dk, float* dv, int batch, int heads, int n,
+                           int causal, float scale, void* workspace, hipStream_t stream);
+
 // Split-KV paged decode: partials into `workspace`, then the merge pass writes o / lse.
 int decode_default_split(int batch, int heads, int max_seq_len);
 size_t decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len, int split);

@@ -88,6 +88,30 @@ def test_decode_validation(kw, status):
     assert dec(**kw) == status
 
 
+def bwd(**kw):
+    a = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, lens=None, dq=FAKE, dk=FAKE,
+             dv=FAKE, B=1, H=1, n=16, d=128, causal=0, scale=0.1, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return attn.lib().attn_bwd(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
+                               a["lens"], a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["n"],
+                               a["d"], a["causal"], a["scale"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(do=None), INVALID),
+    (dict(lse=None), INVALID), (dict(dq=None), INVALID), (dict(dv=None), INVALID),
+    (dict(n=0), INVALID), (dict(scale=float("nan")), INVALID), (dict(d=64), UNSUPPORTED),
+    (dict(dtype=0), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(wsb=63), WORKSPACE),
+])
+def test_bwd_validation(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_bwd_workspace_bytes():
+    assert attn.attn_bwd_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 4
+    assert attn.attn_bwd_workspace_bytes(0, 3, 100) == 0
+
+
 def test_decode_workspace_bytes():
     f = attn.attn_decode_workspace_bytes
     # partials: B * H * ceil(max_seq_len / split) entries of (m, l, u[128]) fp32
