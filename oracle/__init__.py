@@ -18,16 +18,18 @@ Sources (the pages' own text; formulas there are partly garbled by HTML extracti
 
 Functions and their pins (tests/test_oracle.py):
   attention / attend / attention_rows / decode
-      pinned by 50-digit mpmath brute force on tiny inputs, the worked example, row sums,
-      convex hull, shift invariance, closed forms (Q = 0 prefix means, single key,
-      dominant key).
+      pinned by 50-digit mpmath brute force on tiny inputs (also with grouped K/V heads and
+      causal windows), the worked example, row sums, convex hull, shift invariance, closed
+      forms (Q = 0 prefix means, single key, dominant key, a window of one returns the
+      token's own value, a window as long as the sequence is plain causal).
   online_softmax_scalar / merge / summarize / blocked_softmax
       pinned by the worked example's step table (and its wrong variant), the block-merge
       experiment design of el-ai.com section 4, and merge associativity/commutativity.
   attention_grad (backward.py)
       pinned by 50-digit central differences of the forward definition (masks, padding)
-      and by closed forms (sum of dK is zero; sum of dV is the sum of dO; Q = 0 gives
-      dK = 0; single-key rows send no gradient to q or k).
+      (also two query heads sharing one K/V head under a causal window) and by closed forms
+      (sum of dK is zero; sum of dV is the sum of dO; Q = 0 gives dK = 0; single-key rows
+      send no gradient to q or k).
 No function here is "parity unpinned".
 """
 

@@ -11,7 +11,12 @@ the formula and its "softmax" and "V" paragraphs):
     o_i  = sum_j A_ij v_j
 
 Masks: a causal mask gives query i the keys j <= i (maeste.it: future tokens are set to
--inf before the softmax); a length mask of n_b admits queries and keys < n_b only.  The
+-inf before the softmax); a length mask of n_b admits queries and keys < n_b only.  Two
+variants the pages name as complements of exact attention without defining them
+(aimpact.prandi.net FlashAttention page, "Impatto pratico": grouped-query attention and
+sliding-window attention; maeste.it: a sliding window limits each token's reach) are read
+in their plainest form: with H query heads and H_kv key/value heads, query head h uses K/V
+head h // (H / H_kv); a causal window of w admits keys i - w < j <= i.  The
 maximum is subtracted before exponentiating (el-ai.com section 1: it multiplies numerator
 and denominator by the same factor).  A row with no admitted key has no distribution
 (el-ai.com section 5 asks for an explicit convention): its output is 0 and its
@@ -65,24 +70,36 @@ def attend(S: np.ndarray, V: np.ndarray, valid: np.ndarray | None = None):
     return O, lse
 
 
-def _valid(nq: int, nk: int, causal: bool, q_offset: int = 0) -> np.ndarray:
-    """Admitted (query, key) pairs; query row r has absolute position q_offset + r."""
-    if not causal:
-        return np.ones((nq, nk), dtype=bool)
-    qi = np.arange(nq)[:, None] + q_offset
+def _valid(nq: int, nk: int, causal: bool, window: int = 0) -> np.ndarray:
+    """Admitted (query, key) pairs of one square block (query i, key j)."""
+    qi = np.arange(nq)[:, None]
     kj = np.arange(nk)[None, :]
-    return kj <= qi
+    ok = np.ones((nq, nk), dtype=bool)
+    if causal:
+        ok &= kj <= qi
+    if window:
+        ok &= kj > qi - window
+    return ok
 
 
-def attention(q, k, v, *, scale: float | None = None, causal: bool = False, seq_lens=None):
-    """Prefill attention over [B, H, n, d] tensors.
+def _group(H: int, Hkv: int) -> int:
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    return H // Hkv
+
+
+def attention(q, k, v, *, scale: float | None = None, causal: bool = False, seq_lens=None,
+              window: int = 0):
+    """Prefill attention: q [B, H, n, d]; k, v [B, H_kv, n, d] with H a multiple of H_kv.
 
     seq_lens: optional length per batch row (host ints); queries and keys at positions
     >= n_b are padding: their outputs are 0 / lse -inf and they are never read.
+    window: 0 for none, else keys i - window < j (with causal: the last `window` tokens).
     Returns (O [B, H, n, d] fp64, LSE [B, H, n] fp64).
     """
     q, k, v = to_f64(q), to_f64(k), to_f64(v)
     B, H, n, d = q.shape
+    G = _group(H, k.shape[1])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     lens = [n] * B if seq_lens is None else [int(x) for x in seq_lens]
@@ -92,14 +109,15 @@ def attention(q, k, v, *, scale: float | None = None, causal: bool = False, seq_
         L = lens[b]
         if L <= 0:
             continue
-        valid = _valid(L, L, causal)
+        valid = _valid(L, L, causal, window)
         for h in range(H):
-            S = scale * (q[b, h, :L] @ k[b, h, :L].T)
-            O[b, h, :L], LSE[b, h, :L] = attend(S, v[b, h, :L], valid)
+            S = scale * (q[b, h, :L] @ k[b, h // G, :L].T)
+            O[b, h, :L], LSE[b, h, :L] = attend(S, v[b, h // G, :L], valid)
     return O, LSE
 
 
-def attention_rows(q, k, v, rows, *, scale: float | None = None, causal: bool = False, seq_lens=None):
+def attention_rows(q, k, v, rows, *, scale: float | None = None, causal: bool = False, seq_lens=None,
+                   window: int = 0):
     """Attention for selected query rows only (the sampled check of long sequences).
 
     rows: int array [B, H, R] (or [H, R] when B == 1) of query positions.
@@ -107,6 +125,7 @@ def attention_rows(q, k, v, rows, *, scale: float | None = None, causal: bool = 
     """
     q, k, v = to_f64(q), to_f64(k), to_f64(v)
     B, H, n, d = q.shape
+    G = _group(H, k.shape[1])
     rows = np.asarray(rows)
     if rows.ndim == 2:
         rows = rows[None]
@@ -120,20 +139,23 @@ def attention_rows(q, k, v, rows, *, scale: float | None = None, causal: bool = 
         L = lens[b]
         for h in range(H):
             r = rows[b, h]
-            S = scale * (q[b, h, r] @ k[b, h, :L].T)
+            S = scale * (q[b, h, r] @ k[b, h // G, :L].T)
             valid = np.ones((R, L), dtype=bool)
             if causal:
                 valid &= np.arange(L)[None, :] <= r[:, None]
+            if window:
+                valid &= np.arange(L)[None, :] > r[:, None] - window
             valid &= (r < L)[:, None]
-            O[b, h], LSE[b, h] = attend(S, v[b, h, :L], valid)
+            O[b, h], LSE[b, h] = attend(S, v[b, h // G, :L], valid)
     return O, LSE
 
 
-def decode(q, k_seqs, v_seqs, *, scale: float | None = None):
-    """One query per sequence against that sequence's whole cache (no mask inside it).
+def decode(q, k_seqs, v_seqs, *, scale: float | None = None, window: int = 0):
+    """One query per sequence against that sequence's cache.
 
-    q: [B, H, d]; k_seqs / v_seqs: length-B lists of [H, len_b, d] contiguous caches.
-    Returns (O [B, H, d], LSE [B, H]).
+    q: [B, H, d]; k_seqs / v_seqs: length-B lists of [H_kv, len_b, d] contiguous caches.
+    The query sits at position len_b - 1: it admits every cached key, or with a window the
+    keys j > len_b - 1 - window.  Returns (O [B, H, d], LSE [B, H]).
     """
     q = to_f64(q)
     B, H, d = q.shape
@@ -143,8 +165,13 @@ def decode(q, k_seqs, v_seqs, *, scale: float | None = None):
     LSE = np.full((B, H), -np.inf)
     for b in range(B):
         kb, vb = to_f64(k_seqs[b]), to_f64(v_seqs[b])
+        G = _group(H, kb.shape[0])
+        L = kb.shape[1]
+        valid = np.ones((1, L), dtype=bool)
+        if window:
+            valid &= np.arange(L)[None, :] > L - 1 - window
         for h in range(H):
-            S = scale * (q[b, h][None, :] @ kb[h].T)
-            o, lse = attend(S, vb[h])
+            S = scale * (q[b, h][None, :] @ kb[h // G].T)
+            o, lse = attend(S, vb[h // G], valid)
             O[b, h], LSE[b, h] = o[0], lse[0]
     return O, LSE

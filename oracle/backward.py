@@ -24,7 +24,7 @@ import math
 
 import numpy as np
 
-from .attention import to_f64
+from .attention import _group, _valid, to_f64
 
 
 def _probabilities(S: np.ndarray, valid: np.ndarray) -> np.ndarray:
@@ -37,10 +37,12 @@ def _probabilities(S: np.ndarray, valid: np.ndarray) -> np.ndarray:
 
 
 def attention_grad(q, k, v, dout, *, scale: float | None = None, causal: bool = False,
-                   seq_lens=None):
-    """(dQ, dK, dV) of sum(attention(q, k, v) * dout) over [B, H, n, d] tensors."""
+                   seq_lens=None, window: int = 0):
+    """(dQ, dK, dV) of sum(attention(q, k, v) * dout); q, dout [B, H, n, d], k, v
+    [B, H_kv, n, d].  With grouped heads a K/V head's gradient sums over its query heads."""
     q, k, v, dout = to_f64(q), to_f64(k), to_f64(v), to_f64(dout)
     B, H, n, d = q.shape
+    G = _group(H, k.shape[1])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     lens = [n] * B if seq_lens is None else [int(x) for x in seq_lens]
@@ -49,15 +51,14 @@ def attention_grad(q, k, v, dout, *, scale: float | None = None, causal: bool = 
         L = lens[b]
         if L <= 0:
             continue
-        valid = np.ones((L, L), dtype=bool)
-        if causal:
-            valid = np.tril(valid)
+        valid = _valid(L, L, causal, window)
         for h in range(H):
-            Q, K, V, dO = q[b, h, :L], k[b, h, :L], v[b, h, :L], dout[b, h, :L]
+            hk = h // G
+            Q, K, V, dO = q[b, h, :L], k[b, hk, :L], v[b, hk, :L], dout[b, h, :L]
             P = _probabilities(scale * (Q @ K.T), valid)
             dP = dO @ V.T
             dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-            dv[b, h, :L] = P.T @ dO
+            dv[b, hk, :L] += P.T @ dO
             dq[b, h, :L] = scale * (dS @ K)
-            dk[b, h, :L] = scale * (dS.T @ Q)
+            dk[b, hk, :L] += scale * (dS.T @ Q)
     return dq, dk, dv

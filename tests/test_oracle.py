@@ -148,6 +148,70 @@ def test_decode_against_mpmath():
             assert abs(LSE[b, h] - want_lse) <= 1e-13 * max(1.0, abs(want_lse))
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_grouped_heads_and_window_against_mpmath(case):
+    """Query head h reads K/V head h // (H / H_kv); a window w admits keys i - w < j <= i."""
+    rng = np.random.default_rng(2500 + case)
+    H, Hkv = [(4, 1), (4, 2), (6, 3), (2, 2)][case % 4]
+    n, d = int(rng.integers(3, 10)), int(rng.integers(1, 4))
+    window = [1, 2, 3, 100][case % 4] if case < 6 else 0
+    causal = window > 0 or case % 2 == 1
+    q = rng.normal(size=(2, H, n, d)) * 2
+    k = rng.normal(size=(2, Hkv, n, d)) * 2
+    v = rng.normal(size=(2, Hkv, n, d))
+    lens = [n, int(rng.integers(1, n + 1))]
+    O, LSE = oracle.attention(q, k, v, causal=causal, seq_lens=lens, window=window)
+    G = H // Hkv
+    for b in range(2):
+        for h in range(H):
+            for i in range(lens[b]):
+                admitted = [j for j in range(lens[b])
+                            if (not causal or j <= i) and (not window or j > i - window)]
+                want, want_lse = _mp_attention_row(q[b, h, i], k[b, h // G], v[b, h // G],
+                                                   1 / math.sqrt(d), admitted)
+                np.testing.assert_allclose(O[b, h, i], want, rtol=1e-13, atol=1e-14)
+                assert abs(LSE[b, h, i] - want_lse) <= 1e-13 * max(1.0, abs(want_lse))
+            rows = rng.permutation(n)[:3]
+            Or, Lr = oracle.attention_rows(q, k, v, np.broadcast_to(rows, (2, H, 3)), causal=causal,
+                                           seq_lens=lens, window=window)
+            np.testing.assert_array_equal(Or[b, h], np.where((rows < lens[b])[:, None], O[b, h, rows], 0))
+
+
+def test_window_of_one_returns_own_value_and_wide_window_is_causal():
+    rng = np.random.default_rng(8)
+    q, k, v = (rng.normal(size=(1, 2, 7, 3)) for _ in range(3))
+    O, LSE = oracle.attention(q, k, v, causal=True, window=1)
+    np.testing.assert_allclose(O, v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(LSE, np.einsum("bhnd,bhnd->bhn", q, k) / math.sqrt(3), atol=1e-14)
+    Ow, Lw = oracle.attention(q, k, v, causal=True, window=7)
+    Oc, Lc = oracle.attention(q, k, v, causal=True)
+    np.testing.assert_array_equal(Ow, Oc)
+    np.testing.assert_array_equal(Lw, Lc)
+
+
+def test_grouped_heads_reject_a_non_divisor():
+    with pytest.raises(ValueError):
+        oracle.attention(np.zeros((1, 3, 2, 1)), np.zeros((1, 2, 2, 1)), np.zeros((1, 2, 2, 1)))
+
+
+def test_decode_grouped_heads_and_window_against_mpmath():
+    rng = np.random.default_rng(9)
+    B, H, Hkv, d = 3, 4, 2, 3
+    lens = [1, 6, 13]
+    q = rng.normal(size=(B, H, d)) * 3
+    ks = [rng.normal(size=(Hkv, L, d)) * 3 for L in lens]
+    vs = [rng.normal(size=(Hkv, L, d)) for L in lens]
+    for window in (0, 1, 4):
+        O, LSE = oracle.decode(q, ks, vs, window=window)
+        for b in range(B):
+            for h in range(H):
+                lo = lens[b] - window if window else 0
+                want, want_lse = _mp_attention_row(q[b, h], ks[b][h // 2], vs[b][h // 2],
+                                                   1 / math.sqrt(d), range(max(lo, 0), lens[b]))
+                np.testing.assert_allclose(O[b, h], want, rtol=1e-13, atol=1e-14)
+                assert abs(LSE[b, h] - want_lse) <= 1e-13 * max(1.0, abs(want_lse))
+
+
 # ---------------------------------------------------------------- invariants
 def test_rows_are_distributions_and_outputs_in_convex_hull():
     """Rows of A lie in (0,1) and sum to 1; each output is a convex combination of values

@@ -66,6 +66,41 @@ def test_gradients_against_50_digit_finite_differences(case):
         np.testing.assert_allclose(got[0, 0], want, rtol=1e-12, atol=1e-13)
 
 
+def _mp_loss_heads(qs, k, v, dos, scale, window):
+    """sum over query heads of the causal windowed loss, all heads sharing one K/V head."""
+    total = mpmath.mpf(0)
+    n, d = len(k), len(k[0])
+    for q, do in zip(qs, dos):
+        for i in range(n):
+            keys = [j for j in range(n) if j <= i and (not window or j > i - window)]
+            w = [mpmath.exp(scale * mpmath.fsum(q[i][c] * k[j][c] for c in range(d))) for j in keys]
+            den = mpmath.fsum(w)
+            for c in range(len(v[0])):
+                total += mpmath.fsum(wj * v[j][c] for wj, j in zip(w, keys)) / den * do[i][c]
+    return total
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_grouped_window_gradients_against_50_digit_finite_differences(case):
+    """Two query heads on one K/V head: dK and dV sum both heads' contributions."""
+    rng = np.random.default_rng(400 + case)
+    n, d, window = [(4, 2, 2), (5, 2, 3), (3, 3, 0)][case]
+    q = rng.normal(size=(2, n, d)) * 2
+    k = rng.normal(size=(n, d)) * 2
+    v, do = rng.normal(size=(n, d)), rng.normal(size=(2, n, d))
+    dq, dk, dv = oracle.attention_grad(q[None], k[None, None], v[None, None], do[None],
+                                       causal=True, window=window)
+    mp = lambda a: [[mpmath.mpf(float(x)) for x in row] for row in a]
+    mq, mk, mv, mdo = [mp(q[0]), mp(q[1])], mp(k), mp(v), [mp(do[0]), mp(do[1])]
+    msc = mpmath.mpf(1 / math.sqrt(d))
+
+    def f():
+        return _mp_loss_heads(mq, mk, mv, mdo, msc, window)
+
+    for got, x in ((dq[0, 0], mq[0]), (dq[0, 1], mq[1]), (dk[0, 0], mk), (dv[0, 0], mv)):
+        np.testing.assert_allclose(got, _mp_grad(x, f), rtol=1e-12, atol=1e-13)
+
+
 def test_key_sum_and_value_sum_closed_forms():
     """K + 1 w^T leaves every output unchanged, so sum_j dK_j = 0; V + 1 c^T shifts every
     valid output by c, so sum_j dV_j = sum over valid rows of dO_i."""
