@@ -24,6 +24,12 @@
  *   - Unsupported combinations fail loudly with ATTN_ERR_UNSUPPORTED; there is no
  *     fallback path (the-ai.news fused-kernel page, "Attenzione di tipo FlashAttention e
  *     attenzione paginata": forcing a backend that cannot take the input must fail).
+ *   - Grouped key/value heads and a sliding window, the two complements of exact attention
+ *     the aimpact.prandi.net FlashAttention page lists ("Impatto pratico"), are taken in
+ *     their plainest form: `heads` query heads share `kv_heads` K/V heads (heads a multiple
+ *     of kv_heads; query head h reads K/V head h / (heads / kv_heads); kv_heads == heads is
+ *     ordinary multi-head attention), and a window w > 0 limits query i to the keys
+ *     i - w < j <= i (it requires the causal mask; w = 0 means no window).
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -35,7 +41,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -53,8 +59,9 @@ typedef enum attn_dtype {
 /*
  * attn_fwd — prefill attention of every query of every (batch, head).
  *
- * q, k, v, o : [batch, heads, seq_len, head_dim] of `dtype`, contiguous.  o is written
+ * q, o       : [batch, heads, seq_len, head_dim] of `dtype`, contiguous.  o is written
  *              in full (padding rows included) and may not alias q, k or v.
+ * k, v       : [batch, kv_heads, seq_len, head_dim] of `dtype`, contiguous.
  * lse        : optional (NULL allowed) fp32 [batch, heads, seq_len]; receives the natural
  *              log of sum_j exp(scale * <q_i, k_j>) over the admitted keys — the saved
  *              statistic the pages' backward pass recomputes from.
@@ -65,13 +72,17 @@ typedef enum attn_dtype {
  *              Precondition: 1 <= seq_lens[b] <= seq_len.
  * causal     : nonzero => query i admits keys j <= i only (maeste.it: future keys are set
  *              to -inf before the softmax).  Combines with seq_lens.
+ * window     : 0, or w > 0 with causal: query i admits keys i - w < j <= i only.
  * scale      : the factor applied to <q, k>; pass 1/sqrt(head_dim) for the pages' form.
+ * Errors     : ATTN_ERR_INVALID also for kv_heads <= 0, heads % kv_heads != 0, window < 0
+ *              or a window without causal.
  * Supported  : ATTN_F32 with head_dim 64 or 128 (scores accumulated in fp64);
  *              ATTN_BF16 with head_dim 128 (MFMA, fp32 accumulation).
  */
 attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void* v, void* o,
-                     float* lse, const int32_t* seq_lens, int batch, int heads, int seq_len,
-                     int head_dim, int causal, float scale, void* stream);
+                     float* lse, const int32_t* seq_lens, int batch, int heads, int kv_heads,
+                     int seq_len, int head_dim, int causal, int window, float scale,
+                     void* stream);
 
 /*
  * attn_bwd_workspace_bytes — device bytes attn_bwd needs as `workspace` (one fp32 per query
@@ -85,11 +96,14 @@ size_t attn_bwd_workspace_bytes(int batch, int heads, int seq_len);
  * nel Backward Pass"), which keeps only the forward's per-row normalisation statistics and
  * recomputes the weight blocks P_ij = exp(scale <q_i, k_j> - lse_i) from q, k, v.
  *
- * q, k, v, o, dout : [batch, heads, seq_len, head_dim] of `dtype`, contiguous; o and lse
- *              are the outputs attn_fwd produced for these q, k, v, mask and scale.
+ * q, o, dout : [batch, heads, seq_len, head_dim] of `dtype`, contiguous; o and lse are
+ *              the outputs attn_fwd produced for these q, k, v, mask and scale.
+ * k, v       : [batch, kv_heads, seq_len, head_dim] of `dtype`, contiguous.
  * lse        : fp32 [batch, heads, seq_len] (required).
- * seq_lens, causal, scale : as in attn_fwd (same values as the forward call).
- * dq, dk, dv : fp32 [batch, heads, seq_len, head_dim], written in full (padding rows 0).
+ * seq_lens, kv_heads, causal, window, scale : as in attn_fwd (same values as the forward).
+ * dq         : fp32 [batch, heads, seq_len, head_dim], written in full (padding rows 0).
+ * dk, dv     : fp32 [batch, kv_heads, seq_len, head_dim], written in full; a shared K/V
+ *              head receives the sum over the query heads that read it.
  * workspace  : DEVICE buffer of at least attn_bwd_workspace_bytes() bytes, owned by the
  *              caller; contents on entry do not matter.
  * Supported  : ATTN_BF16 with head_dim 128.
@@ -97,16 +111,17 @@ size_t attn_bwd_workspace_bytes(int batch, int heads, int seq_len);
 attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse,
                      const int32_t* seq_lens, float* dq, float* dk, float* dv, int batch,
-                     int heads, int seq_len, int head_dim, int causal, float scale,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     int heads, int kv_heads, int seq_len, int head_dim, int causal,
+                     int window, float scale, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /*
  * attn_decode_workspace_bytes — device bytes attn_decode_paged needs as `workspace` for
- * these sizes and this split length (kv_split tokens per partial; 0 = the library's
- * default).  Returns 0 for sizes attn_decode_paged would reject.
+ * these sizes, this window and this split length (kv_split tokens per partial; 0 = the
+ * library's default).  Returns 0 for arguments attn_decode_paged would reject.
  */
-size_t attn_decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len,
-                                   int kv_split);
+size_t attn_decode_workspace_bytes(int batch, int heads, int kv_heads, int head_dim,
+                                   int max_seq_len, int window, int kv_split);
 
 /*
  * attn_decode_paged — one new query per sequence against that sequence's paged K/V cache
@@ -114,15 +129,18 @@ size_t attn_decode_workspace_bytes(int batch, int heads, int head_dim, int max_s
  *
  * q           : [batch, heads, head_dim] bf16.
  * k_cache,
- * v_cache     : [num_blocks, heads, block_size, head_dim] bf16 pools of fixed-size blocks;
- *               one (block, head) is block_size * head_dim contiguous elements.
+ * v_cache     : [num_blocks, kv_heads, block_size, head_dim] bf16 pools of fixed-size
+ *               blocks; one (block, K/V head) is block_size * head_dim contiguous elements.
+ *               The query heads that share a K/V head are served together, so each cached
+ *               block is read once per K/V head, not once per query head.
  * block_table : DEVICE int32 [batch, max_blocks_per_seq]; entry i of row b is the pool
  *               block holding tokens [i*block_size, (i+1)*block_size) of sequence b (the
  *               block table of the-ai.news page, "attenzione paginata").  Entries past a
  *               sequence's last block are never read.
- * seq_lens    : DEVICE int32 [batch]; the query of sequence b admits its tokens
- *               0 .. seq_lens[b]-1 (no mask inside the cache).  Slots past seq_lens[b] in
- *               the last block are never used, whatever they hold.
+ * seq_lens    : DEVICE int32 [batch]; the query of sequence b sits at position
+ *               seq_lens[b]-1 and admits its tokens 0 .. seq_lens[b]-1 (no mask inside the
+ *               cache), or with window w > 0 only the last w of them.  Slots outside that
+ *               range are never used, whatever they hold.
  *               Preconditions: 1 <= seq_lens[b] <= max_seq_len, every referenced table
  *               entry in [0, num_blocks).
  * o           : [batch, heads, head_dim] bf16 output.
@@ -130,19 +148,23 @@ size_t attn_decode_workspace_bytes(int batch, int heads, int head_dim, int max_s
  * kv_split    : tokens per split-KV partial, a positive multiple of block_size, or 0 for
  *               the library's default.  Each (sequence, head, split) produces a partial
  *               (m, l, u) that a second kernel merges (el-ai.com section 4); the result
- *               does not depend on kv_split beyond rounding.
+ *               does not depend on kv_split beyond rounding.  Splits start at the first
+ *               admitted token.
  * workspace   : DEVICE buffer of at least attn_decode_workspace_bytes(batch, heads,
- *               head_dim, max_seq_len, kv_split) bytes, owned by the caller; its contents on
- *               entry do not matter.  Concurrent calls must not share one workspace.
+ *               kv_heads, head_dim, max_seq_len, window, kv_split) bytes, owned by the
+ *               caller; its contents on entry do not matter.  Concurrent calls must not
+ *               share one workspace.
+ * Errors      : ATTN_ERR_INVALID also for kv_heads <= 0, heads % kv_heads != 0 or
+ *               window < 0.
  * Supported   : ATTN_BF16, head_dim 128, block_size 16.
  */
 attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_table,
                               const int32_t* seq_lens, void* o, float* lse, int batch,
-                              int heads, int head_dim, int block_size, int num_blocks,
-                              int max_blocks_per_seq, int max_seq_len, float scale,
-                              int kv_split, void* workspace, size_t workspace_bytes,
-                              void* stream);
+                              int heads, int kv_heads, int head_dim, int block_size,
+                              int num_blocks, int max_blocks_per_seq, int max_seq_len,
+                              int window, float scale, int kv_split, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* attn_status_str — static, NUL-terminated name of a status code (never NULL). */
 const char* attn_status_str(attn_status status);

@@ -25,18 +25,19 @@ ATTN_F32, ATTN_BF16 = 0, 1
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 SIGNATURES = {
-    "attn_fwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P]),
+    "attn_fwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                      _P]),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "attn_bwd": (
         _I,
-        [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P,
-         ctypes.c_size_t, _P],
+        [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+         _P, ctypes.c_size_t, _P],
     ),
-    "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
     "attn_decode_paged": (
         _I,
-        [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P,
-         ctypes.c_size_t, _P],
+        [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
+         _P, ctypes.c_size_t, _P],
     ),
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
@@ -119,19 +120,31 @@ def _lengths(seq_lens, batch, limit, device, name="seq_lens"):
     return host.to(torch.int32).to(device)
 
 
-def attn_fwd(q, k, v, *, causal=False, scale=None, seq_lens=None, out=None, lse=None,
-             return_lse=False, stream=None):
-    """Prefill attention over [B, H, n, d] tensors (fp32 d in {64,128}; bf16 d = 128).
+def _kv_heads(q, k, v):
+    """K/V head count of q [B, H, n, d] against k, v [B, H_kv, n, d] (H a multiple of H_kv)."""
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, H, n, d]; k and v one shape [B, H_kv, n, d]")
+    B, H, n, d = q.shape
+    Hkv = int(k.shape[1])
+    if (k.shape[0], k.shape[2], k.shape[3]) != (B, n, d) or Hkv < 1 or H % Hkv:
+        raise ValueError("k, v must be [B, H_kv, n, d] with H a multiple of H_kv")
+    return Hkv
+
+
+def attn_fwd(q, k, v, *, causal=False, window=0, scale=None, seq_lens=None, out=None,
+             lse=None, return_lse=False, stream=None):
+    """Prefill attention: q [B, H, n, d], k and v [B, H_kv, n, d] (fp32 d in {64,128};
+    bf16 d = 128).
 
     seq_lens: optional per-batch lengths (host sequence or device int32 tensor); rows past
-    a length are padding (output 0, lse -inf).  Returns o, or (o, lse) with return_lse.
+    a length are padding (output 0, lse -inf).  window > 0 (with causal) limits query i to
+    keys i - window < j <= i.  Returns o, or (o, lse) with return_lse.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(name, t)
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float32 or bfloat16")
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must all be [B, H, n, d] of one shape")
+    Hkv = _kv_heads(q, k, v)
     B, H, n, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -150,7 +163,8 @@ def attn_fwd(q, k, v, *, causal=False, scale=None, seq_lens=None, out=None, lse=
     st = lib().attn_fwd(_DT[q.dtype], q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                         lse.data_ptr() if lse is not None else None,
                         lens.data_ptr() if lens is not None else None,
-                        B, H, n, d, int(bool(causal)), float(scale), _stream(stream))
+                        B, H, Hkv, n, d, int(bool(causal)), int(window), float(scale),
+                        _stream(stream))
     if st != ATTN_OK:
         raise AttnError("attn_fwd", st)
     return (out, lse) if return_lse else out
@@ -160,19 +174,20 @@ def attn_bwd_workspace_bytes(batch, heads, seq_len) -> int:
     return int(lib().attn_bwd_workspace_bytes(batch, heads, seq_len))
 
 
-def attn_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, seq_lens=None, dq=None,
-             dk=None, dv=None, workspace=None, stream=None):
+def attn_bwd(q, k, v, o, dout, lse, *, causal=False, window=0, scale=None, seq_lens=None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Gradients (dq, dk, dv) in fp32 of sum(o * dout), recomputing the weights from lse.
 
-    q, k, v, o, dout: bf16 [B, H, n, 128]; lse: fp32 [B, H, n] from attn_fwd(return_lse=True)
-    with the same mask, lengths and scale.
+    q, o, dout: bf16 [B, H, n, 128]; k, v: bf16 [B, H_kv, n, 128]; lse: fp32 [B, H, n] from
+    attn_fwd(return_lse=True) with the same mask, window, lengths and scale.  dk and dv have
+    the shape of k (a shared K/V head gets the sum over its query heads).
     """
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_dev(name, t, torch.bfloat16)
+    for name, t in (("o", o), ("dout", dout)):
         if t.shape != q.shape:
             raise ValueError(f"{name} must have the shape of q")
-    if q.dim() != 4:
-        raise ValueError("q must be [B, H, n, d]")
+    Hkv = _kv_heads(q, k, v)
     B, H, n, d = q.shape
     _check_dev("lse", lse, torch.float32)
     if lse.shape != (B, H, n):
@@ -180,12 +195,12 @@ def attn_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, seq_lens=None, 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     outs = []
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, t, shape in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, k.shape)):
         if t is None:
-            t = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+            t = torch.empty(shape, dtype=torch.float32, device=q.device)
         _check_dev(name, t, torch.float32)
-        if t.shape != q.shape:
-            raise ValueError(f"{name} must be [B, H, n, d]")
+        if t.shape != shape:
+            raise ValueError(f"{name} must be {tuple(shape)}")
         outs.append(t)
     need = attn_bwd_workspace_bytes(B, H, n)
     if workspace is None:
@@ -194,32 +209,36 @@ def attn_bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, seq_lens=None, 
     lens = _lengths(seq_lens, B, n, q.device)
     st = lib().attn_bwd(ATTN_BF16, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                         dout.data_ptr(), lse.data_ptr(), lens.data_ptr() if lens is not None else None,
-                        outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), B, H, n, d,
-                        int(bool(causal)), float(scale), workspace.data_ptr(),
+                        outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), B, H, Hkv, n,
+                        d, int(bool(causal)), int(window), float(scale), workspace.data_ptr(),
                         workspace.numel() * workspace.element_size(), _stream(stream))
     if st != ATTN_OK:
         raise AttnError("attn_bwd", st)
     return tuple(outs)
 
 
-def attn_decode_workspace_bytes(batch, heads, head_dim, max_seq_len, kv_split=0) -> int:
-    return int(lib().attn_decode_workspace_bytes(batch, heads, head_dim, max_seq_len, kv_split))
+def attn_decode_workspace_bytes(batch, heads, head_dim, max_seq_len, kv_split=0, *,
+                                kv_heads=None, window=0) -> int:
+    kv_heads = heads if kv_heads is None else kv_heads
+    return int(lib().attn_decode_workspace_bytes(batch, heads, kv_heads, head_dim, max_seq_len,
+                                                 window, kv_split))
 
 
-def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, scale=None,
-                      kv_split=0, out=None, lse=None, return_lse=False, workspace=None,
-                      stream=None):
-    """One bf16 query per sequence ([B, H, d]) against a paged cache [blocks, H, 16, d]."""
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, window=0,
+                      scale=None, kv_split=0, out=None, lse=None, return_lse=False,
+                      workspace=None, stream=None):
+    """One bf16 query per sequence ([B, H, d]) against a paged cache [blocks, H_kv, 16, d]
+    (H a multiple of H_kv).  window > 0 admits only each sequence's last `window` tokens."""
     _check_dev("q", q, torch.bfloat16)
     _check_dev("k_cache", k_cache, torch.bfloat16)
     _check_dev("v_cache", v_cache, torch.bfloat16)
     _check_dev("block_table", block_table, torch.int32)
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
-        raise ValueError("q must be [B, H, d]; caches [num_blocks, H, block_size, d]")
+        raise ValueError("q must be [B, H, d]; caches [num_blocks, H_kv, block_size, d]")
     B, H, d = q.shape
-    nb, Hc, bs, dc = k_cache.shape
-    if Hc != H or dc != d:
-        raise ValueError("cache heads / head_dim differ from q")
+    nb, Hkv, bs, dc = k_cache.shape
+    if Hkv < 1 or H % Hkv or dc != d:
+        raise ValueError("cache heads must divide the query heads; head_dim must match q")
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_blocks_per_seq]")
     if seq_lens is None:
@@ -234,7 +253,8 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len
         lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_dev("lse", lse, torch.float32)
-    need = attn_decode_workspace_bytes(B, H, d, max_seq_len, kv_split)
+    need = attn_decode_workspace_bytes(B, H, d, max_seq_len, kv_split, kv_heads=Hkv,
+                                       window=window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check_dev("workspace", workspace)
@@ -242,8 +262,8 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len
     st = lib().attn_decode_paged(
         ATTN_BF16, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
         lens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
-        B, H, d, bs, nb, int(block_table.shape[1]), int(max_seq_len), float(scale),
-        int(kv_split), workspace.data_ptr(), ws_bytes, _stream(stream))
+        B, H, Hkv, d, bs, nb, int(block_table.shape[1]), int(max_seq_len), int(window),
+        float(scale), int(kv_split), workspace.data_ptr(), ws_bytes, _stream(stream))
     if st != ATTN_OK:
         raise AttnError("attn_decode_paged", st)
     return (out, lse) if return_lse else out

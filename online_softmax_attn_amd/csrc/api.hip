@@ -15,9 +15,14 @@ attn_status launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATT
 constexpr int kDecodeBlock = 16;
 constexpr int kDecodeMaxSplit = 64 * kDecodeBlock;  // one table entry per lane of a wave
 
+// grouped heads and window: heads a positive multiple of kv_heads, window >= 0
+bool heads_window_ok(int heads, int kv_heads, int window) {
+  return kv_heads > 0 && heads % kv_heads == 0 && window >= 0;
+}
+
 // the split length attn_decode_paged will use, or 0 if `kv_split` is not acceptable
-int resolve_split(int batch, int heads, int max_seq_len, int kv_split) {
-  if (kv_split == 0) return decode_default_split(batch, heads, max_seq_len);
+int resolve_split(int batch, int heads, int kv_heads, int max_seq_len, int window, int kv_split) {
+  if (kv_split == 0) return decode_default_split(batch, heads, kv_heads, max_seq_len, window);
   if (kv_split < 0 || kv_split % kDecodeBlock != 0 || kv_split > kDecodeMaxSplit) return 0;
   return kv_split;
 }
@@ -40,10 +45,12 @@ const char* attn_status_str(attn_status status) {
 }
 
 attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void* v, void* o,
-                     float* lse, const int32_t* seq_lens, int batch, int heads, int seq_len,
-                     int head_dim, int causal, float scale, void* stream) {
+                     float* lse, const int32_t* seq_lens, int batch, int heads, int kv_heads,
+                     int seq_len, int head_dim, int causal, int window, float scale,
+                     void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID;
   if (batch <= 0 || heads <= 0 || seq_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID;
+  if (!heads_window_ok(heads, kv_heads, window) || (window > 0 && !causal)) return ATTN_ERR_INVALID;
   if (!finite_positive(scale)) return ATTN_ERR_INVALID;
   // 32-bit byte offsets inside one (batch, head) slice
   const long long elem = dtype == ATTN_F32 ? 4 : 2;
@@ -55,14 +62,15 @@ attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void*
     if ((long long)batch * heads >= 65536) return ATTN_ERR_UNSUPPORTED;  // grid.y limit
     return launch_status(launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                         static_cast<const float*>(v), static_cast<float*>(o), lse,
-                                        seq_lens, batch, heads, seq_len, head_dim, causal != 0,
-                                        scale, s));
+                                        seq_lens, batch, heads, kv_heads, seq_len, head_dim,
+                                        causal != 0, window, scale, s));
   }
   if (dtype == ATTN_BF16) {
     if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
     return launch_status(launch_fwd_bf16(static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                                          static_cast<const bf16*>(v), static_cast<bf16*>(o), lse,
-                                         seq_lens, batch, heads, seq_len, causal != 0, scale, s));
+                                         seq_lens, batch, heads, kv_heads, seq_len, causal != 0,
+                                         window, scale, s));
   }
   return ATTN_ERR_UNSUPPORTED;
 }
@@ -75,10 +83,12 @@ size_t attn_bwd_workspace_bytes(int batch, int heads, int seq_len) {
 attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse,
                      const int32_t* seq_lens, float* dq, float* dk, float* dv, int batch,
-                     int heads, int seq_len, int head_dim, int causal, float scale,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     int heads, int kv_heads, int seq_len, int head_dim, int causal,
+                     int window, float scale, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_INVALID;
   if (batch <= 0 || heads <= 0 || seq_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID;
+  if (!heads_window_ok(heads, kv_heads, window) || (window > 0 && !causal)) return ATTN_ERR_INVALID;
   if (!finite_positive(scale)) return ATTN_ERR_INVALID;
   if (dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   // 32-bit byte offsets inside one (batch, head) slice; one fp32 gradient row is 512 bytes
@@ -89,42 +99,45 @@ attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void*
   return launch_status(launch_bwd_bf16(
       static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
       static_cast<const bf16*>(o), static_cast<const bf16*>(dout), lse, seq_lens, dq, dk, dv,
-      batch, heads, seq_len, causal != 0, scale, workspace, reinterpret_cast<hipStream_t>(stream)));
+      batch, heads, kv_heads, seq_len, causal != 0, window, scale, workspace,
+      reinterpret_cast<hipStream_t>(stream)));
 }
 
-size_t attn_decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len,
-                                   int kv_split) {
+size_t attn_decode_workspace_bytes(int batch, int heads, int kv_heads, int head_dim,
+                                   int max_seq_len, int window, int kv_split) {
   if (batch <= 0 || heads <= 0 || head_dim != 128 || max_seq_len <= 0) return 0;
-  const int split = resolve_split(batch, heads, max_seq_len, kv_split);
+  if (!heads_window_ok(heads, kv_heads, window)) return 0;
+  const int split = resolve_split(batch, heads, kv_heads, max_seq_len, window, kv_split);
   if (split == 0) return 0;
-  return decode_workspace_bytes(batch, heads, head_dim, max_seq_len, split);
+  return decode_workspace_bytes(batch, heads, head_dim, max_seq_len, window, split);
 }
 
 attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_table,
                               const int32_t* seq_lens, void* o, float* lse, int batch,
-                              int heads, int head_dim, int block_size, int num_blocks,
-                              int max_blocks_per_seq, int max_seq_len, float scale,
-                              int kv_split, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              int heads, int kv_heads, int head_dim, int block_size,
+                              int num_blocks, int max_blocks_per_seq, int max_seq_len,
+                              int window, float scale, int kv_split, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o) return ATTN_ERR_INVALID;
   if (batch <= 0 || heads <= 0 || head_dim <= 0 || num_blocks <= 0 || max_seq_len <= 0)
     return ATTN_ERR_INVALID;
   if (block_size <= 0 || max_blocks_per_seq <= 0) return ATTN_ERR_INVALID;
+  if (!heads_window_ok(heads, kv_heads, window)) return ATTN_ERR_INVALID;
   if (!finite_positive(scale)) return ATTN_ERR_INVALID;
   if (dtype != ATTN_BF16 || head_dim != 128 || block_size != kDecodeBlock)
     return ATTN_ERR_UNSUPPORTED;
   if ((long long)max_blocks_per_seq * block_size < max_seq_len) return ATTN_ERR_INVALID;
   if (batch > 65535 || heads > 65535) return ATTN_ERR_UNSUPPORTED;  // grid.y / grid.z limits
-  const int split = resolve_split(batch, heads, max_seq_len, kv_split);
+  const int split = resolve_split(batch, heads, kv_heads, max_seq_len, window, kv_split);
   if (split == 0) return ATTN_ERR_INVALID;
-  const size_t need = decode_workspace_bytes(batch, heads, head_dim, max_seq_len, split);
+  const size_t need = decode_workspace_bytes(batch, heads, head_dim, max_seq_len, window, split);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   return launch_status(launch_decode_paged(
       static_cast<const bf16*>(q), static_cast<const bf16*>(k_cache),
       static_cast<const bf16*>(v_cache), block_table, seq_lens, static_cast<bf16*>(o), lse,
-      batch, heads, num_blocks, max_blocks_per_seq, max_seq_len, scale, split, workspace,
-      reinterpret_cast<hipStream_t>(stream)));
+      batch, heads, kv_heads, num_blocks, max_blocks_per_seq, max_seq_len, window, scale, split,
+      workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

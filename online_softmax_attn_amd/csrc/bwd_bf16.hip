@@ -17,6 +17,11 @@
 // the B operand as bf16, and the transposed A operands (K^T for dQ; dO^T and Q^T for dK/dV)
 // come from row-major LDS tiles through ds_read_b64_tr_b16.  Masked pairs get weight 0 by
 // selection, so padding never enters a sum whatever it holds.
+//
+// Grouped K/V heads: dQ reads the shared K/V slice; one dK/dV workgroup sweeps the query
+// tiles of every query head of its group in turn, so the sum over the group stays in
+// registers (no atomics, no second pass).  A causal window w narrows both sweeps to the
+// pairs i - w < j <= i.
 #include "common.h"
 
 namespace {
@@ -112,8 +117,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restric
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    const int32_t* __restrict__ lens, float* __restrict__ dQ, int B, int H, int n,
-    int n_qtiles, int causal, float c_log2, float scale) {
+    const int32_t* __restrict__ lens, float* __restrict__ dQ, int B, int H, int Hkv, int n,
+    int n_qtiles, int causal, int window, float c_log2, float scale) {
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][kTileElems];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[2][kTileElems];
   constexpr int kBM = 128;
@@ -123,6 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int bh = blockIdx.x % HB;
   const int L = clamp_len(lens, bh / H, n);
   const size_t base = (size_t)bh * n * kD;
+  const size_t kv_base = ((size_t)(bh / H) * Hkv + (bh % H) / (H / Hkv)) * n * kD;
   const int m0 = qt * kBM;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hl = lane >> 5, lq = lane & 31;
   const int qi = m0 + 32 * w + lq;
@@ -137,8 +143,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   const uint32_t valid_bytes = (uint32_t)L * kD * 2;
   const rsrc_t rq = make_rsrc(Q + base, valid_bytes);
-  const rsrc_t rk = make_rsrc(K + base, valid_bytes);
-  const rsrc_t rv = make_rsrc(V + base, valid_bytes);
+  const rsrc_t rk = make_rsrc(K + kv_base, valid_bytes);
+  const rsrc_t rv = make_rsrc(V + kv_base, valid_bytes);
   const rsrc_t rg = make_rsrc(dO + base, valid_bytes);
 
   bf16x8 qop[8], gop[8];  // Q^T and dO^T operands: dims 16 ks + 8 hl .. +7 of query qi
@@ -152,7 +158,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const float Di = row_ok ? Dv[(size_t)bh * n + qi] : 0.f;
 
   const int kend = causal ? min(L, m0 + kBM) : L;
-  const int n_tiles = (kend + kTile - 1) / kTile;
+  const int n_tiles = (kend + kTile - 1) / kTile;  // tiles [t_first, n_tiles); tile t in buffer t & 1
+  const int t_first = window ? max(0, m0 - window + 1) / kTile : 0;
   const int wave_q_first = m0 + 32 * w, wave_q_last = wave_q_first + 31;
   const int wave_tiles = causal ? min(n_tiles, wave_q_last / kTile + 1) : n_tiles;
   const TileFill fill(w, lane);
@@ -163,12 +170,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  fill.issue(rk, Ks[0], 0, w);
-  fill.issue(rv, Vs[0], 0, w);
+  fill.issue(rk, Ks[t_first & 1], t_first, w);
+  fill.issue(rv, Vs[t_first & 1], t_first, w);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = t_first; t < n_tiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) {
       fill.issue(rk, Ks[buf ^ 1], t + 1, w);
@@ -195,7 +202,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[ks], s[kb], 0, 0, 0);
           dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gop[ks], dp[kb], 0, 0, 0);
         }
-      const bool need_mask = !row_ok || (k0 + kTile > L) || (causal && k0 + kTile - 1 > wave_q_first);
+      const bool need_mask = !row_ok || (k0 + kTile > L) || (causal && k0 + kTile - 1 > wave_q_first) ||
+                             (window && k0 <= wave_q_last - window);
       bf16x8 dsop[4];
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -lse2));
             if (need_mask) {
               const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-              const bool ok = row_ok && key < L && (!causal || key <= qi);
+              const bool ok = row_ok && key < L && (!causal || key <= qi) && (!window || key > qi - window);
               p = ok ? p : 0.f;
             }
             d2[u] = p * (dp[kb][r] - Di);
@@ -249,18 +257,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     const int32_t* __restrict__ lens, float* __restrict__ dK, float* __restrict__ dV, int B,
-    int H, int n, int causal, float c_log2, float scale) {
+    int H, int Hkv, int n, int causal, int window, float c_log2, float scale) {
   __shared__ __attribute__((aligned(1024))) bf16 Qs[2][kTileElems];
   __shared__ __attribute__((aligned(1024))) bf16 Gs[2][kTileElems];
   __shared__ __attribute__((aligned(16))) float Ls[2][kTile];  // log2-unit LSE; +inf on padding
   __shared__ __attribute__((aligned(16))) float Ds[2][kTile];
   constexpr int kBK = 128;
 
-  const int HB = H * B;
+  const int HB = Hkv * B;
   const int kt = (int)(blockIdx.x / HB);  // key block 0 has the most causal work: first
-  const int bh = blockIdx.x % HB;
-  const int L = clamp_len(lens, bh / H, n);
-  const size_t base = (size_t)bh * n * kD;
+  const int bhk = blockIdx.x % HB;        // b * Hkv + K/V head
+  const int b = bhk / Hkv, G = H / Hkv;
+  const int bh0 = b * H + (bhk % Hkv) * G;  // first query head of the group
+  const int L = clamp_len(lens, b, n);
+  const size_t kv_base = (size_t)bhk * n * kD;
   const int k0 = kt * kBK;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hl = lane >> 5, lq = lane & 31;
   const int kj = k0 + 32 * w + lq;  // this lane's key
@@ -269,18 +279,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     for (int i = tid; i < kBK * kD / 4; i += kThreads) {
       const int r = k0 + (i * 4) / kD;
       if (r < n) {
-        *reinterpret_cast<floatx4*>(dK + base + (size_t)r * kD + (i * 4) % kD) = floatx4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<floatx4*>(dV + base + (size_t)r * kD + (i * 4) % kD) = floatx4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<floatx4*>(dK + kv_base + (size_t)r * kD + (i * 4) % kD) = floatx4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<floatx4*>(dV + kv_base + (size_t)r * kD + (i * 4) % kD) = floatx4{0.f, 0.f, 0.f, 0.f};
       }
     }
     return;
   }
 
   const uint32_t valid_bytes = (uint32_t)L * kD * 2;
-  const rsrc_t rq = make_rsrc(Q + base, valid_bytes);
-  const rsrc_t rk = make_rsrc(K + base, valid_bytes);
-  const rsrc_t rv = make_rsrc(V + base, valid_bytes);
-  const rsrc_t rg = make_rsrc(dO + base, valid_bytes);
+  const rsrc_t rk = make_rsrc(K + kv_base, valid_bytes);
+  const rsrc_t rv = make_rsrc(V + kv_base, valid_bytes);
 
   bf16x8 kop[8], vop[8];  // K^T and V^T operands of this lane's key
 #pragma unroll
@@ -291,12 +299,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const bool key_ok = kj < L;
   const int wave_k_first = k0 + 32 * w, wave_k_last = wave_k_first + 31;
 
+  // query tiles [t0, t1) of each of the G query heads, swept head after head: step `it`
+  // is tile t0 + it % nt of head it / nt
   const int t0 = causal ? k0 / kTile : 0;  // first query tile that admits any key here
-  const int t1 = (L + kTile - 1) / kTile;
+  const int qend = window ? min(L, k0 + kBK - 1 + window) : L;  // later queries admit none
+  const int t1 = (qend + kTile - 1) / kTile;
+  const int nt = t1 - t0;
+  const int steps = G * nt;
   const TileFill fill(w, lane);
-  auto issue = [&](int t, int buf) {
-    fill.issue(rq, Qs[buf], t, w);
-    fill.issue(rg, Gs[buf], t, w);
+  auto issue = [&](int it, int buf) {
+    const int bh = bh0 + it / nt, t = t0 + it % nt;
+    const size_t base = (size_t)bh * n * kD;
+    fill.issue(make_rsrc(Q + base, valid_bytes), Qs[buf], t, w);
+    fill.issue(make_rsrc(dO + base, valid_bytes), Gs[buf], t, w);
     if (tid < kTile) {
       const int q = t * kTile + tid;
       Ls[buf][tid] = q < L ? LSE[(size_t)bh * n + q] * ATTN_LOG2E : INFINITY;
@@ -313,19 +328,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       av[db][r] = 0.f;
     }
 
-  issue(t0, 0);
+  issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
-    if (t + 1 < t1) issue(t + 1, buf ^ 1);
+  for (int it = 0; it < steps; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < steps) issue(it + 1, buf ^ 1);
+    const int t = t0 + it % nt;
     const bf16* Qt = Qs[buf];
     const bf16* Gt = Gs[buf];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int q0 = t * kTile + 32 * qb;
       if (causal && q0 + 31 < wave_k_first) continue;  // every query of the block precedes every key
+      if (window && q0 - wave_k_last >= window) continue;  // every query is past every key's window
       floatx16 s, dp;  // S and dP: lane holds query q0 + 8 (r/4) + 4 hl + r%4 of key kj
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -339,7 +356,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[ks], dp, 0, 0, 0);
       }
-      const bool need_mask = !key_ok || (k0 + kBK > L) || (causal && q0 < wave_k_last);
+      const bool need_mask = !key_ok || (k0 + kBK > L) || (causal && q0 < wave_k_last) ||
+                             (window && q0 + 31 - wave_k_first >= window);
       bf16x8 pop[2], dsop[2];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
@@ -352,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
           float p = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l4[c]));  // 0 on padding rows
           if (need_mask) {
             const int q = q0 + 8 * a + 4 * hl + c;
-            const bool ok = key_ok && (!causal || kj <= q);
+            const bool ok = key_ok && (!causal || kj <= q) && (!window || kj > q - window);
             p = ok ? p : 0.f;
           }
           p4[c] = p;
@@ -380,8 +398,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
 
   if (kj < n) {
-    float* krow = dK + base + (size_t)kj * kD;
-    float* vrow = dV + base + (size_t)kj * kD;
+    float* krow = dK + kv_base + (size_t)kj * kD;
+    float* vrow = dV + kv_base + (size_t)kj * kD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -406,8 +424,9 @@ size_t bwd_workspace_bytes(int batch, int heads, int n) {
 
 hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
                            const bf16* dout, const float* lse, const int32_t* seq_lens,
-                           float* dq, float* dk, float* dv, int batch, int heads, int n,
-                           int causal, float scale, void* workspace, hipStream_t stream) {
+                           float* dq, float* dk, float* dv, int batch, int heads, int kv_heads,
+                           int n, int causal, int window, float scale, void* workspace,
+                           hipStream_t stream) {
   float* Dv = static_cast<float*>(workspace);
   const long long rows = (long long)batch * heads * n;
   const unsigned pre_blocks = (unsigned)((rows * 16 + kThreads - 1) / kThreads);
@@ -418,13 +437,13 @@ hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf
   const float c_log2 = scale * ATTN_LOG2E;
   const int n_qtiles = (n + 127) / 128;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)n_qtiles * batch * heads), dim3(kThreads), 0,
-                     stream, q, k, v, dout, lse, Dv, seq_lens, dq, batch, heads, n, n_qtiles,
-                     causal, c_log2, scale);
+                     stream, q, k, v, dout, lse, Dv, seq_lens, dq, batch, heads, kv_heads, n,
+                     n_qtiles, causal, window, c_log2, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_ktiles = (n + 127) / 128;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)n_ktiles * batch * heads), dim3(kThreads), 0,
-                     stream, q, k, v, dout, lse, Dv, seq_lens, dk, dv, batch, heads, n, causal,
-                     c_log2, scale);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)n_ktiles * batch * kv_heads), dim3(kThreads),
+                     0, stream, q, k, v, dout, lse, Dv, seq_lens, dk, dv, batch, heads, kv_heads,
+                     n, causal, window, c_log2, scale);
   return hipGetLastError();
 }

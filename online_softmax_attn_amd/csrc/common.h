@@ -17,31 +17,34 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 #define ATTN_LN2 0.6931471805599453f
 
 // Launchers (host side).  Arguments are already validated by the C ABI layer; each returns
-// the HIP status of its launch(es).
+// the HIP status of its launch(es).  `kv_heads` divides `heads` (query head h reads K/V head
+// h / (heads / kv_heads)); `window` is 0 or a causal window length.
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          const int32_t* seq_lens, int batch, int heads, int n, int head_dim,
-                          int causal, float scale, hipStream_t stream);
+                          const int32_t* seq_lens, int batch, int heads, int kv_heads, int n,
+                          int head_dim, int causal, int window, float scale, hipStream_t stream);
 
 hipError_t launch_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* lse,
-                           const int32_t* seq_lens, int batch, int heads, int n, int causal,
-                           float scale, hipStream_t stream);
+                           const int32_t* seq_lens, int batch, int heads, int kv_heads, int n,
+                           int causal, int window, float scale, hipStream_t stream);
 
 // Backward pass (bf16 in, fp32 gradients): D = rowsum(dO * O) into `workspace`, then dQ
 // and dK/dV kernels that recompute the weights from the saved log-sum-exp.
 size_t bwd_workspace_bytes(int batch, int heads, int n);
 hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
                            const bf16* dout, const float* lse, const int32_t* seq_lens,
-                           float* dq, float* dk, float* dv, int batch, int heads, int n,
-                           int causal, float scale, void* workspace, hipStream_t stream);
+                           float* dq, float* dk, float* dv, int batch, int heads, int kv_heads,
+                           int n, int causal, int window, float scale, void* workspace,
+                           hipStream_t stream);
 
 // Split-KV paged decode: partials into `workspace`, then the merge pass writes o / lse.
-int decode_default_split(int batch, int heads, int max_seq_len);
-size_t decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len, int split);
+int decode_default_split(int batch, int heads, int kv_heads, int max_seq_len, int window);
+size_t decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len, int window,
+                              int split);
 hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v_cache,
                                const int32_t* block_table, const int32_t* seq_lens, bf16* o,
-                               float* lse, int batch, int heads, int num_blocks,
-                               int max_blocks_per_seq, int max_seq_len, float scale, int split,
-                               void* workspace, hipStream_t stream);
+                               float* lse, int batch, int heads, int kv_heads, int num_blocks,
+                               int max_blocks_per_seq, int max_seq_len, int window, float scale,
+                               int split, void* workspace, hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------
 // Buffer resources: loads through a buffer descriptor return 0 for any byte offset at or

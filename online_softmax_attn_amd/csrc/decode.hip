@@ -83,28 +83,40 @@ struct Block {
   uint4 k[4], v[4];  // token 4 i + lane/16, dims 8 (lane%16) .. +7
 };
 
+// One wave per (sequence, K/V head, split, group of GQ query heads).  The GQ query heads
+// share the K/V head, so every block loaded is scored and accumulated GQ times: with
+// grouped heads the cache is read once per K/V head.  Tokens [kbeg, L) are admitted
+// (kbeg > 0 under a window); splits count blocks from the one holding kbeg.
+template <int GQ>
 __global__ __launch_bounds__(64) void decode_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, void* __restrict__ ws,
-    int H, int num_blocks, int max_blocks_per_seq, int max_seq_len, int max_splits,
-    int split_blocks, float c_log2, size_t n_part) {
+    int H, int Hkv, int num_blocks, int max_blocks_per_seq, int max_seq_len, int window,
+    int max_splits, int split_blocks, float c_log2, size_t n_part) {
   // heads fastest: waves dispatched together read neighbouring 4 KiB pieces of one block
-  const int h = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  const int chunks = H / Hkv / GQ;  // query-head groups per K/V head
+  const int hk = blockIdx.x / chunks;
+  const int h0 = hk * (H / Hkv) + (blockIdx.x % chunks) * GQ;  // first query head served
+  const int split = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int L = min(max(lens[b], 0), max_seq_len);  // out-of-contract lengths stay in bounds
+  const int kbeg = window ? max(L - window, 0) : 0;
   const int nblk = (L + kBlock - 1) / kBlock;
-  const int blk0 = split * split_blocks;
+  const int blk0 = kbeg / kBlock + split * split_blocks;
   if (blk0 >= nblk) return;  // beyond this sequence: the merge never reads it
   const int count = min(blk0 + split_blocks, nblk) - blk0;
   const int grp = lane >> 4, dc = lane & 15;
 
-  // this lane's 8 query dims as bf16 pairs
-  const uint4 qv = *reinterpret_cast<const uint4*>(q + ((size_t)b * H + h) * kD + 8 * dc);
+  // this lane's 8 dims of each served query, as bf16 pairs
+  uint4 qv[GQ];
+#pragma unroll
+  for (int g = 0; g < GQ; ++g)
+    qv[g] = *reinterpret_cast<const uint4*>(q + ((size_t)b * H + h0 + g) * kD + 8 * dc);
   // table slice for this split: lane j holds entry blk0 + j
   const int tbl = (lane < count) ? table[(size_t)b * max_blocks_per_seq + blk0 + lane] : 0;
 
-  const size_t blk_stride = (size_t)H * kBlock * kD;
-  const size_t lane_off = (size_t)h * kBlock * kD + (size_t)grp * kD + 8 * dc;
+  const size_t blk_stride = (size_t)Hkv * kBlock * kD;
+  const size_t lane_off = (size_t)hk * kBlock * kD + (size_t)grp * kD + 8 * dc;
   auto fetch = [&](int j, Block& d) {
     // out-of-contract block ids are clamped into the pool rather than read out of bounds
     const int phys = min(max(__builtin_amdgcn_readlane(tbl, j), 0), num_blocks - 1);
@@ -116,52 +128,69 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     for (int i = 0; i < 4; ++i) d.v[i] = load_stream(vp + 4 * i * kD);
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
-  float acc[8];
+  float m_run[GQ], l_run[GQ], acc[GQ][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int g = 0; g < GQ; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
+  }
 
   auto consume = [&](int j, const Block& d) {
-    float s[4];
+    const int tok0 = (blk0 + j) * kBlock + grp;  // token of score i is tok0 + 4 i
+    const bool edge = (blk0 + j + 1) * kBlock > L || (blk0 + j) * kBlock < kbeg;
+    bool ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok[i] = !edge || (tok0 + 4 * i < L && tok0 + 4 * i >= kbeg);
+    float vf[4][8];  // V as fp32, shared by the served heads
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(&d.k[i]);
-      const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qv);
-      float x = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw[e]),
-                                            __builtin_bit_cast(bf16x2, qw[e]), x, false);
-      s[i] = row_sum16(x);
-    }
-    const int tok0 = (blk0 + j) * kBlock + grp;  // token of s[i] is tok0 + 4 i
-    const bool tail = (blk0 + j + 1) * kBlock > L;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = (!tail || tok0 + 4 * i < L) ? s[i] * c_log2 : -INFINITY;
-      mx = __builtin_fmaxf(mx, s[i]);
-    }
-    mx = max32(max16(mx));
-    // every block holds at least one admitted token, so mx and m_new are finite
-    const float m_new = __builtin_fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
-    l_run = fmaf(l_run, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] *= alpha;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // a slot past the sequence end never enters the sum, whatever it holds
-      if (tail && tok0 + 4 * i >= L) continue;
       const uint32_t* vw = reinterpret_cast<const uint32_t*>(&d.v[i]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = fmaf(p[i], bf_lo(vw[e]), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(p[i], bf_hi(vw[e]), acc[2 * e + 1]);
+        vf[i][2 * e] = bf_lo(vw[e]);
+        vf[i][2 * e + 1] = bf_hi(vw[e]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      float s[4];
+      const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qv[g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t* kw = reinterpret_cast<const uint32_t*>(&d.k[i]);
+        float x = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw[e]),
+                                              __builtin_bit_cast(bf16x2, qw[e]), x, false);
+        s[i] = row_sum16(x);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = ok[i] ? s[i] * c_log2 : -INFINITY;
+        mx = __builtin_fmaxf(mx, s[i]);
+      }
+      mx = max32(max16(mx));
+      // every block holds at least one admitted token, so mx and m_new are finite
+      const float m_new = __builtin_fmaxf(m_run[g], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+      m_run[g] = m_new;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = ok[i] ? __builtin_amdgcn_exp2f(s[i] - m_new) : 0.f;
+      l_run[g] = fmaf(l_run[g], alpha, (p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[g][c] *= alpha;
+      // a slot outside the admitted range has p = 0 by selection, so whatever it holds
+      // (NaN included) is never multiplied in
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!ok[i]) continue;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[g][c] = fmaf(p[i], vf[i][c], acc[g][c]);
       }
     }
   };
@@ -183,25 +212,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   for (int r = 0; r <= kDepth; ++r)
     if (j + r < count) consume(j + r, buf[r]);
 
-  // reduce over the four 16-lane groups (each lane summed its own tokens)
-  l_run = xor32(xor16(l_run));
-#pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = xor32(xor16(acc[c]));
   const Partials P = partial_views(ws, n_part);
-  const size_t p = ((size_t)b * H + h) * max_splits + split;
-  if (lane < 16) {
-    float* u = P.u + p * kD + 8 * dc;
-    floatx4 lo, hi;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      lo[c] = acc[c];
-      hi[c] = acc[4 + c];
-    }
-    *reinterpret_cast<floatx4*>(u) = lo;
-    *reinterpret_cast<floatx4*>(u + 4) = hi;
-    if (lane == 0) {
-      P.m[p] = m_run;
-      P.l[p] = l_run;
+  for (int g = 0; g < GQ; ++g) {
+    // reduce over the four 16-lane groups (each lane summed its own tokens)
+    const float l_tot = xor32(xor16(l_run[g]));
+    float a[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a[c] = xor32(xor16(acc[g][c]));
+    const size_t p = ((size_t)b * H + h0 + g) * max_splits + split;
+    if (lane < 16) {
+      float* u = P.u + p * kD + 8 * dc;
+      floatx4 lo, hi;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        lo[c] = a[c];
+        hi[c] = a[4 + c];
+      }
+      *reinterpret_cast<floatx4*>(u) = lo;
+      *reinterpret_cast<floatx4*>(u + 4) = hi;
+      if (lane == 0) {
+        P.m[p] = m_run[g];
+        P.l[p] = l_tot;
+      }
     }
   }
 }
@@ -209,12 +242,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 // merge of the partial summaries of one (sequence, head): one wave, lane = 2 dimensions
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const void* __restrict__ ws, const int32_t* __restrict__ lens, bf16* __restrict__ o,
-    float* __restrict__ lse, int H, int max_seq_len, int max_splits, int split_tokens,
-    size_t n_part) {
+    float* __restrict__ lse, int H, int max_seq_len, int window, int max_splits,
+    int split_blocks, size_t n_part) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
   const int L = min(max(lens[b], 0), max_seq_len);
-  const int ns = (L + split_tokens - 1) / split_tokens;
+  const int kbeg = window ? max(L - window, 0) : 0;
+  const int nblk = (L + kBlock - 1) / kBlock - kbeg / kBlock;  // blocks the splits cover
+  const int ns = (nblk + split_blocks - 1) / split_blocks;
   const size_t out = ((size_t)b * H + h) * kD + 2 * lane;
   if (ns == 0) {  // no admitted key (out of contract): the empty-row convention
     o[out] = (bf16)0.f;
@@ -245,41 +280,73 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   if (lse && lane == 0) lse[(size_t)b * H + h] = mstar * ATTN_LN2 + __logf(lsum);
 }
 
+// Blocks a sequence's admitted tokens can touch: all of them, or under a window of w the
+// w tokens [L - w, L), which straddle at most ceil((w + 15) / 16) blocks.
+int span_blocks(int max_seq_len, int window) {
+  const int all = (max_seq_len + kBlock - 1) / kBlock;
+  return window ? min(all, (window + 2 * kBlock - 2) / kBlock) : all;
+}
+
+int max_splits_for(int max_seq_len, int window, int split) {
+  const int split_blocks = split / kBlock;
+  return (span_blocks(max_seq_len, window) + split_blocks - 1) / split_blocks;
+}
+
+// Query heads one wave serves: the largest of 8, 4, 2, 1 that divides the group size.
+int heads_per_wave(int heads, int kv_heads) {
+  const int G = heads / kv_heads;
+  return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+}
+
 }  // namespace
 
 // Split length: as long as possible (each split wave streams its blocks back to back) while
 // the grid still offers enough waves to keep every CU's memory pipeline full.  Measured on
 // the decode workload (B=32, H=32, lengths up to 8192): 128 tokens 407 us, 256: 390 us,
 // 512: 376 us, 768: 376 us, 1024: 378 us.
-int decode_default_split(int batch, int heads, int max_seq_len) {
+int decode_default_split(int batch, int heads, int kv_heads, int max_seq_len, int window) {
   constexpr long long kTargetWaves = 8192;
+  const long long wave_heads = (long long)heads / heads_per_wave(heads, kv_heads);
+  const long long span = (long long)span_blocks(max_seq_len, window) * kBlock;
   for (int split : {512, 256, 128}) {
-    const long long waves = (long long)batch * heads * ((max_seq_len + split - 1) / split);
+    const long long waves = (long long)batch * wave_heads * ((span + split - 1) / split);
     if (waves >= kTargetWaves) return split;
   }
   return 64;
 }
 
-size_t decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len, int split) {
-  const size_t max_splits = (size_t)((max_seq_len + split - 1) / split);
-  const size_t n_part = (size_t)batch * heads * max_splits;
+size_t decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len, int window,
+                              int split) {
+  const size_t n_part = (size_t)batch * heads * max_splits_for(max_seq_len, window, split);
   return n_part * (2 + (size_t)head_dim) * sizeof(float);
 }
 
 hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v_cache,
                                const int32_t* block_table, const int32_t* seq_lens, bf16* o,
-                               float* lse, int batch, int heads, int num_blocks,
-                               int max_blocks_per_seq, int max_seq_len, float scale, int split,
-                               void* workspace, hipStream_t stream) {
-  const int max_splits = (max_seq_len + split - 1) / split;
+                               float* lse, int batch, int heads, int kv_heads, int num_blocks,
+                               int max_blocks_per_seq, int max_seq_len, int window, float scale,
+                               int split, void* workspace, hipStream_t stream) {
+  const int max_splits = max_splits_for(max_seq_len, window, split);
   const size_t n_part = (size_t)batch * heads * max_splits;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(heads, max_splits, batch), dim3(64), 0, stream,
-                     q, k_cache, v_cache, block_table, seq_lens, workspace, heads, num_blocks,
-                     max_blocks_per_seq, max_seq_len, max_splits, split / kBlock,
-                     scale * ATTN_LOG2E, n_part);
+  const int gq = heads_per_wave(heads, kv_heads);
+  const dim3 grid((unsigned)(heads / gq), (unsigned)max_splits, (unsigned)batch);
+  const float c_log2 = scale * ATTN_LOG2E;
+#define ATTN_DECODE_LAUNCH(GQ)                                                                  \
+  hipLaunchKernelGGL(decode_split_kernel<GQ>, grid, dim3(64), 0, stream, q, k_cache, v_cache,   \
+                     block_table, seq_lens, workspace, heads, kv_heads, num_blocks,             \
+                     max_blocks_per_seq, max_seq_len, window, max_splits, split / kBlock,       \
+                     c_log2, n_part)
+  switch (gq) {
+    case 8: ATTN_DECODE_LAUNCH(8); break;
+    case 4: ATTN_DECODE_LAUNCH(4); break;
+    case 2: ATTN_DECODE_LAUNCH(2); break;
+    default: ATTN_DECODE_LAUNCH(1); break;
+  }
+#undef ATTN_DECODE_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(heads, batch), dim3(64), 0, stream, workspace,
-                     seq_lens, o, lse, heads, max_seq_len, max_splits, split, n_part);
+                     seq_lens, o, lse, heads, max_seq_len, window, max_splits, split / kBlock,
+                     n_part);
   return hipGetLastError();
 }

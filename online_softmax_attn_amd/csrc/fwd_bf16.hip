@@ -28,6 +28,11 @@
 //   * causal: tiles strictly above a wave's diagonal are skipped, the grid is issued
 //     heaviest-first, and every query tile of one (batch, head) lands on the same XCD
 //     (workgroups are dealt round-robin to the 8 XCDs) so K/V are re-read from one L2.
+//     Consecutive heads share an XCD too, so the query heads of one K/V group (grouped
+//     heads) read their shared K/V from one L2 as well.
+//   * causal window w: the key loop starts at the first tile any query of the workgroup
+//     admits (query i admits keys i - w < j <= i); tiles that cross a window edge are
+//     masked like the diagonal ones.
 #include "common.h"
 
 namespace {
@@ -74,20 +79,26 @@ struct Tile {
   floatx16 s[2];  // S^T of 64 keys: lane holds key 32 kb + 8 (r/4) + 4 hl + r%4 of query lq
 };
 
+// kWindow: a causal window is in force (`window` > 0); without it the window terms compile
+// away and the register budget of the plain kernel is untouched.
+template <bool kWindow>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ lens, int B,
-    int H, int n, int n_qtiles, int causal, float c_log2) {
+    int H, int Hkv, int n, int n_qtiles, int causal, int window, float c_log2) {
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][kTileElems];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[2][kTileElems];
 
   const int HB = H * B;
   const int qt = n_qtiles - 1 - (int)(blockIdx.x / HB);  // heaviest causal tiles first
-  const int bh = blockIdx.x % HB;
+  // slot j runs on XCD j % 8; give each XCD a contiguous range of (batch, head)s
+  const int j = blockIdx.x % HB;
+  const int bh = (HB % 8 == 0) ? (j % 8) * (HB / 8) + j / 8 : j;
   const int b = bh / H;
   int L = lens ? lens[b] : n;
   L = L < 0 ? 0 : (L > n ? n : L);
   const size_t base = (size_t)bh * n * kD;
+  const size_t kv_base = ((size_t)b * Hkv + (bh % H) / (H / Hkv)) * n * kD;
   const int m0 = qt * kBM;
 
   const int tid = threadIdx.x;
@@ -110,8 +121,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // rows >= L read as zeros through the descriptors' range
   const uint32_t valid_bytes = (uint32_t)L * kD * 2;
   const rsrc_t rq = make_rsrc(Q + base, valid_bytes);
-  const rsrc_t rk = make_rsrc(K + base, valid_bytes);
-  const rsrc_t rv = make_rsrc(V + base, valid_bytes);
+  const rsrc_t rk = make_rsrc(K + kv_base, valid_bytes);
+  const rsrc_t rv = make_rsrc(V + kv_base, valid_bytes);
 
   // Q^T operand: lane (query lq, half hl) holds dims 16*ks + 8*hl .. +7 for ks = 0..7.
   bf16x8 qop[8];
@@ -119,7 +130,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   for (int ks = 0; ks < 8; ++ks) qop[ks] = load_b128(rq, (qi * kD + 16 * ks + 8 * hl) * 2);
 
   const int kend = causal ? min(L, m0 + kBM) : L;
-  const int n_tiles = (kend + kBN - 1) / kBN;
+  const int n_tiles = (kend + kBN - 1) / kBN;                 // tiles [t_first, n_tiles)
+  const int t_first = kWindow ? max(0, m0 - window + 1) / kBN : 0;
   const int wave_q_first = m0 + w * 32;
   const int wave_q_last = wave_q_first + 31;
   // tiles a wave takes part in (causal: none strictly above its diagonal)
@@ -188,13 +200,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool ok = key < L && (!causal || key <= qi);
+        const bool ok = key < L && (!causal || key <= qi) && (!kWindow || key > qi - window);
         T.s[kb][r] = ok ? T.s[kb][r] : -INFINITY;
       }
   };
   auto need_mask = [&](int t) {
     const int k0 = t * kBN;
-    return (k0 + kBN > L) || (causal && k0 + kBN - 1 > wave_q_first);
+    return (k0 + kBN > L) || (causal && k0 + kBN - 1 > wave_q_first) ||
+           (kWindow && k0 <= wave_q_last - window);
   };
   auto row_max = [&](const Tile& T) {  // scaled (log2 units) max over this tile's 64 keys
     float mx = __builtin_fmaxf(T.s[0][0], T.s[0][1]);
@@ -300,19 +313,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     __syncthreads();
   };
 
-  // ---- prologue: K(0), V(0), K(1) in flight; scores and max of tile 0
-  issue_k(0, 0);
-  issue_v(0, 0);
-  if (n_tiles > 1) issue_k(1, 1);
+  // ---- prologue: K(t0), V(t0), K(t0+1) in flight; scores and max of tile t0.  Tile t
+  // always lives in buffer t & 1.
+  const int t0 = t_first;
+  issue_k(t0, t0 & 1);
+  issue_v(t0, t0 & 1);
+  if (t0 + 1 < n_tiles) issue_k(t0 + 1, (t0 + 1) & 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Tile ta, tb;
-  compute_s(ta, Ks[0]);
-  if (need_mask(0)) apply_mask(ta, 0);
+  compute_s(ta, Ks[t0 & 1]);
+  if (need_mask(t0)) apply_mask(ta, t0 * kBN);
   raise_ref(row_max(ta));
-  __syncthreads();  // every wave is done with K(0) before K(2) overwrites its buffer
+  __syncthreads();  // every wave is done with K(t0) before K(t0+2) overwrites its buffer
 
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = t0; t < n_tiles; t += 2) {
     step(t, ta, tb);
     if (t + 1 < n_tiles) step(t + 1, tb, ta);
   }
@@ -341,11 +356,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 }  // namespace
 
 hipError_t launch_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* lse,
-                           const int32_t* seq_lens, int batch, int heads, int n, int causal,
-                           float scale, hipStream_t stream) {
+                           const int32_t* seq_lens, int batch, int heads, int kv_heads, int n,
+                           int causal, int window, float scale, hipStream_t stream) {
   const int n_qtiles = (n + kBM - 1) / kBM;
   const dim3 grid((unsigned)n_qtiles * batch * heads);
-  hipLaunchKernelGGL(fwd_bf16_kernel, grid, dim3(kThreads), 0, stream, q, k, v, o, lse,
-                     seq_lens, batch, heads, n, n_qtiles, causal, scale * ATTN_LOG2E);
+  if (window > 0)
+    hipLaunchKernelGGL(fwd_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, q, k, v, o, lse,
+                       seq_lens, batch, heads, kv_heads, n, n_qtiles, causal, window,
+                       scale * ATTN_LOG2E);
+  else
+    hipLaunchKernelGGL(fwd_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, q, k, v, o, lse,
+                       seq_lens, batch, heads, kv_heads, n, n_qtiles, causal, 0,
+                       scale * ATTN_LOG2E);
   return hipGetLastError();
 }

@@ -14,7 +14,8 @@
 // (batch, head); each query is served by TPQ = head_dim / 32 threads that each hold 32 of
 // its dimensions (query slice, accumulator slice) and combine partial dot products with
 // lane shuffles.  K and V stream through LDS in tiles of 32 keys.  This path exists for
-// exactness, not speed: its workloads are small.
+// exactness, not speed: its workloads are small.  Grouped K/V heads only change which K/V
+// slice is read; a causal window only narrows each query's admitted key range.
 #include "common.h"
 
 namespace {
@@ -30,8 +31,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
                                                            float* __restrict__ O,
                                                            float* __restrict__ LSE,
                                                            const int32_t* __restrict__ lens,
-                                                           int H, int n, int causal,
-                                                           double scale) {
+                                                           int H, int Hkv, int n, int causal,
+                                                           int window, double scale) {
   constexpr int TPQ = D / kSlice;        // threads per query
   constexpr int QPB = kThreads / TPQ;    // queries per workgroup
   __shared__ float Ks[kTileKeys * D];
@@ -43,6 +44,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   int L = lens ? lens[b] : n;
   L = L < 0 ? 0 : (L > n ? n : L);
   const size_t base = (size_t)bh * n * D;
+  const size_t kv_base = ((size_t)b * Hkv + (bh % H) / (H / Hkv)) * n * D;
 
   const int tid = threadIdx.x;
   const int qi = q0 + tid / TPQ;
@@ -61,17 +63,19 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   // keys any row of this workgroup can admit
   int kend = L;
   if (causal) kend = min(kend, q0 + QPB);
+  const int kbeg = window ? max(0, q0 - window + 1) : 0;
   const int kmax = row_valid ? (causal ? min(qi, L - 1) : L - 1) : -1;  // last admitted key
+  const int kmin = window ? qi - window + 1 : 0;                       // first admitted key
 
-  for (int k0 = 0; k0 < kend; k0 += kTileKeys) {
+  for (int k0 = kbeg; k0 < kend; k0 += kTileKeys) {
     // cooperative fp32 tile load; keys past L are zero-filled and never admitted
     for (int i = tid; i < kTileKeys * D / 4; i += kThreads) {
       const int row = (i * 4) / D, col = (i * 4) % D;
       const int key = k0 + row;
       float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
       if (key < L) {
-        kk = *reinterpret_cast<const float4*>(K + base + (size_t)key * D + col);
-        vv = *reinterpret_cast<const float4*>(V + base + (size_t)key * D + col);
+        kk = *reinterpret_cast<const float4*>(K + kv_base + (size_t)key * D + col);
+        vv = *reinterpret_cast<const float4*>(V + kv_base + (size_t)key * D + col);
       }
       *reinterpret_cast<float4*>(Ks + row * D + col) = kk;
       *reinterpret_cast<float4*>(Vs + row * D + col) = vv;
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 #pragma unroll
       for (int off = 1; off < TPQ; off <<= 1) s += __shfl_xor(s, off);
       s *= scale;
-      if (k0 + j <= kmax) {
+      if (k0 + j <= kmax && k0 + j >= kmin) {
         const float* vrow = Vs + j * D + part * kSlice;
         if (s > m) {
           const double a = exp(m - s);  // rescales l and u together; 0 on the first key
@@ -122,17 +126,17 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          const int32_t* seq_lens, int batch, int heads, int n, int head_dim,
-                          int causal, float scale, hipStream_t stream) {
+                          const int32_t* seq_lens, int batch, int heads, int kv_heads, int n,
+                          int head_dim, int causal, int window, float scale, hipStream_t stream) {
   const dim3 block(kThreads);
   if (head_dim == 64) {
     const dim3 grid((n + 127) / 128, batch * heads);
     hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, block, 0, stream, q, k, v, o, lse, seq_lens,
-                       heads, n, causal, (double)scale);
+                       heads, kv_heads, n, causal, window, (double)scale);
   } else {
     const dim3 grid((n + 63) / 64, batch * heads);
     hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, block, 0, stream, q, k, v, o, lse, seq_lens,
-                       heads, n, causal, (double)scale);
+                       heads, kv_heads, n, causal, window, (double)scale);
   }
   return hipGetLastError();
 }

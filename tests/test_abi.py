@@ -46,11 +46,12 @@ def test_status_strings():
 
 
 def fwd(**kw):
-    a = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, lens=None, B=1, H=1, n=16,
-             d=128, causal=0, scale=0.1)
+    a = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, lens=None, B=1, H=1, Hkv=1,
+             n=16, d=128, causal=0, window=0, scale=0.1)
     a.update(kw)
     return attn.lib().attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["lens"],
-                               a["B"], a["H"], a["n"], a["d"], a["causal"], a["scale"], None)
+                               a["B"], a["H"], a["Hkv"], a["n"], a["d"], a["causal"], a["window"],
+                               a["scale"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -60,6 +61,9 @@ def fwd(**kw):
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(d=64), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(dtype=0, d=96), UNSUPPORTED),
     (dict(dtype=7), UNSUPPORTED), (dict(n=1 << 24, d=128), UNSUPPORTED),
+    (dict(Hkv=0), INVALID), (dict(H=4, Hkv=3), INVALID), (dict(H=4, Hkv=8), INVALID),
+    (dict(window=-1, causal=1), INVALID), (dict(window=8, causal=0), INVALID),
+    (dict(H=4, Hkv=2, window=8, causal=1, d=96), UNSUPPORTED),
 ])
 def test_fwd_validation(kw, status):
     assert fwd(**kw) == status
@@ -67,12 +71,13 @@ def test_fwd_validation(kw, status):
 
 def dec(**kw):
     a = dict(dtype=1, q=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, lens=FAKE, o=FAKE, lse=None, B=2, H=4,
-             d=128, bs=16, nb=10, mb=8, msl=128, scale=0.1, split=0, ws=FAKE, wsb=1 << 30)
+             Hkv=4, d=128, bs=16, nb=10, mb=8, msl=128, window=0, scale=0.1, split=0, ws=FAKE,
+             wsb=1 << 30)
     a.update(kw)
     return attn.lib().attn_decode_paged(a["dtype"], a["q"], a["kc"], a["vc"], a["tbl"], a["lens"],
-                                        a["o"], a["lse"], a["B"], a["H"], a["d"], a["bs"], a["nb"],
-                                        a["mb"], a["msl"], a["scale"], a["split"], a["ws"], a["wsb"],
-                                        None)
+                                        a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["d"], a["bs"],
+                                        a["nb"], a["mb"], a["msl"], a["window"], a["scale"],
+                                        a["split"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -83,6 +88,7 @@ def dec(**kw):
     (dict(split=24), INVALID), (dict(split=-16), INVALID), (dict(split=2048), INVALID),
     (dict(bs=32, mb=4), UNSUPPORTED), (dict(d=64), UNSUPPORTED), (dict(dtype=0), UNSUPPORTED),
     (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE),
+    (dict(Hkv=0), INVALID), (dict(Hkv=3), INVALID), (dict(window=-5), INVALID),
 ])
 def test_decode_validation(kw, status):
     assert dec(**kw) == status
@@ -90,11 +96,13 @@ def test_decode_validation(kw, status):
 
 def bwd(**kw):
     a = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, lens=None, dq=FAKE, dk=FAKE,
-             dv=FAKE, B=1, H=1, n=16, d=128, causal=0, scale=0.1, ws=FAKE, wsb=1 << 20)
+             dv=FAKE, B=1, H=1, Hkv=1, n=16, d=128, causal=0, window=0, scale=0.1, ws=FAKE,
+             wsb=1 << 20)
     a.update(kw)
     return attn.lib().attn_bwd(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
-                               a["lens"], a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["n"],
-                               a["d"], a["causal"], a["scale"], a["ws"], a["wsb"], None)
+                               a["lens"], a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["Hkv"],
+                               a["n"], a["d"], a["causal"], a["window"], a["scale"], a["ws"],
+                               a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -102,6 +110,7 @@ def bwd(**kw):
     (dict(lse=None), INVALID), (dict(dq=None), INVALID), (dict(dv=None), INVALID),
     (dict(n=0), INVALID), (dict(scale=float("nan")), INVALID), (dict(d=64), UNSUPPORTED),
     (dict(dtype=0), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(wsb=63), WORKSPACE),
+    (dict(H=2, Hkv=4), INVALID), (dict(window=4), INVALID), (dict(window=-1, causal=1), INVALID),
 ])
 def test_bwd_validation(kw, status):
     assert bwd(**kw) == status
@@ -123,3 +132,11 @@ def test_decode_workspace_bytes():
     assert f(0, 4, 128, 1000, 0) == 0
     need = f(2, 4, 128, 128, 0)
     assert dec(wsb=need - 1) == WORKSPACE
+    # a window of w tokens touches at most ceil((w + 15) / 16) blocks: 300 -> 19 blocks,
+    # 2 splits of 256 tokens instead of 4 for the whole 1000
+    assert f(2, 4, 128, 1000, 256, window=300) == 2 * 4 * 2 * 130 * 4
+    assert f(2, 4, 128, 1000, 256, window=5000) == f(2, 4, 128, 1000, 256)
+    assert f(2, 4, 128, 1000, 256, kv_heads=3) == 0
+    assert f(2, 4, 128, 1000, 256, window=-1) == 0
+    need = f(2, 4, 128, 128, 0, kv_heads=2, window=40)
+    assert need > 0 and dec(Hkv=2, window=40, wsb=need - 1) == WORKSPACE

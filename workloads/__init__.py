@@ -44,20 +44,22 @@ def _cast(x: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
 
 # --------------------------------------------------------------------------- prefill
 def prefill(B, H, n, d, *, dtype=torch.bfloat16, seed=0, qk_scale=1.0, v_uniform=None,
-            lens=None, poison=False):
-    """Q, K, V of shape [B, H, n, d] drawn in the order Q, K, V.
+            lens=None, poison=False, kv_heads=None):
+    """Q [B, H, n, d], then K and V [B, kv_heads, n, d] (kv_heads defaults to H), drawn in
+    the order Q, K, V.
 
     qk_scale multiplies the N(0,1) draws of Q and K; v_uniform=a draws V ~ U(-a, a)
     instead of N(0,1).  lens (optional, host ints) marks positions >= n_b as padding;
     with poison=True those positions of Q, K and V are set to NaN after the draws.
     """
     g = _gen(seed)
+    Hkv = H if kv_heads is None else int(kv_heads)
     q = torch.randn(B, H, n, d, generator=g) * qk_scale
-    k = torch.randn(B, H, n, d, generator=g) * qk_scale
+    k = torch.randn(B, Hkv, n, d, generator=g) * qk_scale
     if v_uniform is None:
-        v = torch.randn(B, H, n, d, generator=g)
+        v = torch.randn(B, Hkv, n, d, generator=g)
     else:
-        v = torch.rand(B, H, n, d, generator=g) * (2 * v_uniform) - v_uniform
+        v = torch.rand(B, Hkv, n, d, generator=g) * (2 * v_uniform) - v_uniform
     q, k, v = _cast(q, dtype), _cast(k, dtype), _cast(v, dtype)
     if poison and lens is not None:
         for b, L in enumerate(lens):
@@ -104,9 +106,9 @@ def long_prefill(seed=5, rows_per_head=64):
 @dataclass
 class PagedDecode:
     q: torch.Tensor            # [B, H, d]
-    k_seqs: list               # B tensors [H, len_b, d] (contiguous, for the oracle)
+    k_seqs: list               # B tensors [H_kv, len_b, d] (contiguous, for the oracle)
     v_seqs: list
-    k_cache: torch.Tensor      # [num_blocks, H, block_size, d]
+    k_cache: torch.Tensor      # [num_blocks, H_kv, block_size, d]
     v_cache: torch.Tensor
     block_table: torch.Tensor  # int32 [B, max_blocks_per_seq], -1 past a sequence's end
     seq_lens: torch.Tensor     # int32 [B]
@@ -123,10 +125,11 @@ class PagedDecode:
 
 
 def paged(lens, H, d, *, seed=0, block_size=16, dtype=torch.bfloat16, max_seq_len=None,
-          poison=False, spare_blocks=0):
+          poison=False, spare_blocks=0, kv_heads=None):
     """One query per sequence and a paged K/V pool holding each sequence's cache.
 
-    Draw order: Q [B,H,d]; then for each sequence b: K_b [H,len_b,d], V_b [H,len_b,d];
+    Draw order: Q [B,H,d]; then for each sequence b: K_b [H_kv,len_b,d], V_b [H_kv,len_b,d]
+    (H_kv = kv_heads, default H);
     then a permutation of the pool's blocks.  Logical block i of sequence b (in the order
     sequence 0's blocks, sequence 1's blocks, ...) is stored at the physical block the
     permutation gives.  Slots past a sequence's length in its last block hold 0 (NaN with
@@ -136,7 +139,7 @@ def paged(lens, H, d, *, seed=0, block_size=16, dtype=torch.bfloat16, max_seq_le
     if max_seq_len is None:
         max_seq_len = max(lens)
     return _paged_from(_gen(seed), lens, H, d, block_size, max_seq_len=max_seq_len,
-                       poison=poison, dtype=dtype, spare_blocks=spare_blocks)
+                       poison=poison, dtype=dtype, spare_blocks=spare_blocks, kv_heads=kv_heads)
 
 
 def paged_decode(seed=4, poison=False):
@@ -151,9 +154,10 @@ def paged_decode(seed=4, poison=False):
 
 
 def _paged_from(g, lens, H, d, block_size, *, max_seq_len, poison=False, dtype=torch.bfloat16,
-                spare_blocks=0):
+                spare_blocks=0, kv_heads=None):
     B = len(lens)
     q = _cast(torch.randn(B, H, d, generator=g), dtype)
+    H = H if kv_heads is None else int(kv_heads)  # the cache holds the K/V heads
     k_seqs, v_seqs = [], []
     for L in lens:
         k_seqs.append(_cast(torch.randn(H, L, d, generator=g), dtype))
