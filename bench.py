@@ -18,6 +18,12 @@ oracle timed on this host over a bounded sample of the prefill workload.
                   times attn_bwd on the [4, 32, 2048, 128] causal workload (dO ~ N(0,1)),
                   in algorithmic TFLOP/s: the five products QK^T, dO V^T, P^T dO, dS K,
                   dS^T Q over the admitted pairs, 2.5x the forward's count.
+--workload grouped
+                  the same two legs with 8 K/V heads for the 32 query heads (grouped heads:
+                  K/V and the decode cache are 4x smaller; the flop count is unchanged).
+--workload window the two legs with a causal window of 1024 tokens: prefill over
+                  [1, 32, 16384, 128] (flops of the admitted pairs only) and the decode
+                  workload reading each sequence's last 1024 tokens.
 --profile-pass    runs one 1 GiB device copy, one prefill and one decode and exits (the
                   command the rocprofv3 counter and trace runs wrap).
 --record-traffic FETCH_CSV WRITE_CSV
@@ -68,16 +74,24 @@ def recorded_traffic(kind):
     return rec.get("bytes_per_launch")
 
 
-def causal_flops(B, H, n, d):
-    return 4.0 * d * B * H * n * (n + 1) / 2
+def causal_flops(B, H, n, d, window=0):
+    """4 d flops (QK^T and PV) per admitted pair; a window admits min(i + 1, w) keys."""
+    if not window or window >= n:
+        return 4.0 * d * B * H * n * (n + 1) / 2
+    pairs = window * (window + 1) / 2 + (n - window) * window
+    return 4.0 * d * B * H * pairs
 
 
-def decode_bytes(w, H, d):
-    toks = int(w.seq_lens.sum())
-    kv = toks * H * d * 2 * 2
-    qo = 2 * w.q.numel() * 2
-    table = sum(math.ceil(int(L) / w.block_size) for L in w.seq_lens) * 4
-    return kv + qo + table
+def decode_bytes(w, H_kv, d, window=0):
+    """Admitted K/V tokens of every K/V head, the query and output, the table entries read."""
+    bs = w.block_size
+    kv = q_o = table = 0
+    for L in (int(x) for x in w.seq_lens):
+        lo = max(L - window, 0) if window else 0
+        kv += (L - lo) * H_kv * d * 2 * 2
+        table += (math.ceil(L / bs) - lo // bs) * 4
+    q_o = 2 * w.q.numel() * 2
+    return kv + q_o + table
 
 
 def cpu_baseline(q, k, v, budget_s=12.0):
@@ -199,7 +213,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["prefill", "long", "backward"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "long", "backward", "grouped", "window"],
+                    default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     args = ap.parse_args()
@@ -221,36 +236,57 @@ def main():
 
     if args.workload == "backward":
         return bench_backward(args)
+    window, kv_heads = 0, 32
+    dec_cfg = " + paged decode B=32 H=32 d=128 lens U[1024,8192] block 16"
     if args.workload == "long":
         w = workloads.long_prefill()
-        B, H, n, d = w["q"].shape
         pre_cfg = "causal prefill B=1 H=32 n=32768 d=128 bf16"
+    elif args.workload == "grouped":
+        kv_heads = 8
+        q3, k3, v3 = workloads.prefill(4, 32, 2048, 128, seed=3, kv_heads=kv_heads)
+        w = dict(q=q3, k=k3, v=v3)
+        pre_cfg = "causal prefill B=4 H=32 H_kv=8 n=2048 d=128 bf16"
+        dec_cfg = " + paged decode B=32 H=32 H_kv=8 d=128 lens U[1024,8192] block 16"
+    elif args.workload == "window":
+        window = 1024
+        q3, k3, v3 = workloads.prefill(1, 32, 16384, 128, seed=6)
+        w = dict(q=q3, k=k3, v=v3)
+        pre_cfg = "causal window-1024 prefill B=1 H=32 n=16384 d=128 bf16"
+        dec_cfg = " + paged decode B=32 H=32 d=128 lens U[1024,8192] window 1024 block 16"
     else:
         w = workloads.causal_prefill()
-        B, H, n, d = w["q"].shape
         pre_cfg = "causal prefill B=4 H=32 n=2048 d=128 bf16"
+    B, H, n, d = w["q"].shape
     q_cpu, k_cpu, v_cpu = w["q"], w["k"], w["v"]
     q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
     o = torch.empty_like(q)
-    flops = causal_flops(B, H, n, d)
+    flops = causal_flops(B, H, n, d, window)
 
     dec = None
-    if args.workload == "prefill":
-        pw = workloads.paged_decode()
+    if args.workload in ("prefill", "grouped", "window"):
+        if kv_heads == 32:
+            pw = workloads.paged_decode()
+        else:  # the decode workload's lengths, K/V drawn for kv_heads heads
+            g = torch.Generator().manual_seed(4)
+            dl = [int(x) for x in torch.randint(1024, 8193, (32,), generator=g)]
+            pw = workloads.paged(dl, 32, 128, seed=44, max_seq_len=8192, kv_heads=kv_heads)
         dq = pw.q.to(dev)
         kc, vc = pw.k_cache.to(dev), pw.v_cache.to(dev)
         tbl, lens = pw.block_table.to(dev), pw.seq_lens.to(dev)
         do = torch.empty_like(dq)
-        ws = torch.empty(attn.attn_decode_workspace_bytes(32, 32, 128, pw.max_seq_len), dtype=torch.uint8, device=dev)
-        dbytes = decode_bytes(pw, 32, 128)
+        ws = torch.empty(attn.attn_decode_workspace_bytes(32, 32, 128, pw.max_seq_len,
+                                                          kv_heads=kv_heads, window=window),
+                         dtype=torch.uint8, device=dev)
+        dbytes = decode_bytes(pw, kv_heads, 128, window)
         dec = (dq, kc, vc, tbl, lens, do, ws, pw.max_seq_len)
 
     def prefill():
-        attn.attn_fwd(q, k, v, causal=True, out=o)
+        attn.attn_fwd(q, k, v, causal=True, window=window, out=o)
 
     def decode():
         dq, kc, vc, tbl, lens, do, ws, msl = dec
-        attn.attn_decode_paged(dq, kc, vc, tbl, lens, max_seq_len=msl, out=do, workspace=ws)
+        attn.attn_decode_paged(dq, kc, vc, tbl, lens, max_seq_len=msl, window=window, out=do,
+                               workspace=ws)
 
     if args.profile_pass:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -300,9 +336,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V, seeded KV lengths and page permutation)",
-        "config": {"workload": pre_cfg + (" + paged decode B=32 H=32 d=128 lens U[1024,8192] "
-                                          "block 16" if dec else ""),
-                   "batch": B, "heads": H, "seq_len": n, "head_dim": d, "causal": True},
+        "config": {"workload": pre_cfg + (dec_cfg if dec else ""),
+                   "batch": B, "heads": H, "kv_heads": kv_heads, "seq_len": n, "head_dim": d,
+                   "causal": True, "window": window},
         "prefill": {"ms_avg": round(pre_avg, 5), "ms_min": round(min(pre_ms), 5),
                     "tflops": round(achieved, 2), "frac_of_peak": round(achieved / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -317,9 +353,10 @@ def main():
             "value": round(gbs, 1), "unit": "GB/s", "ms_avg": round(dec_avg, 5),
             "ms_min": round(min(dec_ms), 5), "bytes": dbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic("decode")},
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": recorded_traffic("decode") if args.workload == "prefill" else None},
         }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "prefill":
         result["cpu_baseline"] = cpu_baseline(q_cpu, k_cpu, v_cpu)
     print(json.dumps(result))
 
