@@ -30,14 +30,22 @@ Functions and their pins (tests/test_oracle.py):
       (also two query heads sharing one K/V head under a causal window) and by closed forms
       (sum of dK is zero; sum of dV is the sum of dO; Q = 0 gives dK = 0; single-key rows
       send no gradient to q or k).
+  fp8.e4m3_round / e4m3_encode / quantize_blocks / attention_fp8 (fp8.py)
+      pinned in tests/test_oracle_fp8.py by the E4M3 grid decoded from its bit fields,
+      brute-force nearest rounding with ties to even, torch's float8_e4m3fn cast, block
+      quantisation identities, the Q = 0 closed form, hand-computed two-key examples of the
+      weight rounding and of the once-per-tile running maximum, key-order invariance inside
+      a tile, and the E4M3 error bound against exact attention.
 No function here is "parity unpinned".
 """
 
+from . import fp8
 from .attention import attend, attention, attention_rows, decode, to_f64
 from .backward import attention_grad
 from .online import blocked_softmax, merge, online_softmax_scalar, summarize
 
 __all__ = [
+    "fp8",
     "attend",
     "attention",
     "attention_rows",
