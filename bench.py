@@ -24,6 +24,9 @@ oracle timed on this host over a bounded sample of the prefill workload.
 --workload window the two legs with a causal window of 1024 tokens: prefill over
                   [1, 32, 16384, 128] (flops of the admitted pairs only) and the decode
                   workload reading each sequence's last 1024 tokens.
+--workload fp8    the causal prefill [4, 32, 2048, 128] on FP8 E4M3 operands (attn_fwd_fp8) after
+                  one block quantisation of Q, K, V (attn_quantize_fp8, timed apart); the
+                  roofline is the dense fp8 MFMA peak.
 --profile-pass    runs one 1 GiB device copy, one prefill and one decode and exits (the
                   command the rocprofv3 counter and trace runs wrap).
 --record-traffic FETCH_CSV WRITE_CSV
@@ -46,6 +49,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "online_softmax_attn_amd", "csrc")
@@ -205,6 +209,57 @@ def bench_backward(args):
         "ms_avg": round(ms, 5)}))
 
 
+def bench_fp8(args):
+    import torch
+
+    import online_softmax_attn_amd as attn
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.causal_prefill()
+    B, H, n, d = w["q"].shape
+    q, k, v = w["q"].to(dev), w["k"].to(dev), w["v"].to(dev)
+
+    def quantize():
+        return (attn.attn_quantize_fp8(q), attn.attn_quantize_fp8(k),
+                attn.attn_quantize_fp8(v, transpose=True))
+
+    (q8, sq), (k8, sk), (v8, sv) = quantize()
+    o = torch.empty(B, H, n, d, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        attn.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=True, out=o)
+
+    for _ in range(args.warmup):
+        quantize()
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        quantize()
+        e[1].record()
+        step()
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    flops = causal_flops(B, H, n, d)
+    tf = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "attn fwd TFLOPS (causal prefill, FP8 E4M3 operands, per-block scales)",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3",
+        "data": "synthetic (seeded N(0,1) Q/K/V, bf16 then block-quantised)",
+        "config": {"workload": "causal prefill B=4 H=32 n=2048 d=128, E4M3 operands, bf16 output"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
+        "ms_avg": round(ms, 5), "quantize_ms_avg": round(q_ms, 5)}))
+
+
 def main():
     if len(sys.argv) == 4 and sys.argv[1] == "--record-traffic":
         record_traffic(sys.argv[2], sys.argv[3])
@@ -213,7 +268,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["prefill", "long", "backward", "grouped", "window"],
+    ap.add_argument("--workload", choices=["prefill", "long", "backward", "grouped", "window", "fp8"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -236,6 +291,8 @@ def main():
 
     if args.workload == "backward":
         return bench_backward(args)
+    if args.workload == "fp8":
+        return bench_fp8(args)
     window, kv_heads = 0, 32
     dec_cfg = " + paged decode B=32 H=32 d=128 lens U[1024,8192] block 16"
     if args.workload == "long":

@@ -166,6 +166,49 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_cac
                               int window, float scale, int kv_split, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * attn_quantize_fp8 — block quantisation of a bf16 tensor to FP8 E4M3, the operand format of
+ * attn_fwd_fp8.  The FP8 section of the aimpact.prandi.net FlashAttention page
+ * ("Quantizzazione a Blocchi e Scaling Algebrico") gives each block X the scale
+ * s = max|X| / 448 and the codes clip(round(X / s), -448, 448); here a block is 64 rows of
+ * one (batch, head), X / s is a correctly rounded fp32 division, and rounding is to nearest,
+ * ties to even.  A block that is all 0 gets s = 0 and codes 0.
+ *
+ * x         : bf16 [batch, heads, seq_len, head_dim], contiguous.
+ * x8        : E4M3 codes (OCP E4M3: 1-4-3, bias 7, no infinities), written in full:
+ *             transpose = 0: [batch, heads, seq_len, head_dim] (Q and K);
+ *             transpose = 1: [batch, heads, head_dim, n_pad] with n_pad = 64*ceil(seq_len/64)
+ *             (V, the layout attn_fwd_fp8 reads; the padding columns are 0).
+ * scales    : fp32 [batch, heads, ceil(seq_len / 64)].
+ * seq_lens  : optional DEVICE int32 [batch]; rows at or past a length count as 0 (code 0).
+ * Supported : head_dim 128.
+ */
+attn_status attn_quantize_fp8(const void* x, void* x8, float* scales, const int32_t* seq_lens,
+                              int batch, int heads, int seq_len, int head_dim, int transpose,
+                              void* stream);
+
+/*
+ * attn_fwd_fp8 — prefill attention on E4M3 operands with per-block scales (FP8 section of the
+ * aimpact.prandi.net FlashAttention page): scores (scale * s_Q * s_K) * (Q8 K8^T) accumulated
+ * in fp32; maximum, differences and exponentials in fp32; the weights rounded to E4M3 before
+ * the P.V product (fp32 accumulation); l sums the rounded weights; o = u / l cast to bf16.
+ * The running maximum moves once per 64-key tile (the quantisation block), exactly.
+ *
+ * q8, q_scale : [batch, heads, seq_len, head_dim] codes and fp32 [batch, heads, nb] scales,
+ *               nb = ceil(seq_len / 64), as attn_quantize_fp8 writes them (transpose = 0).
+ * k8, k_scale : [batch, kv_heads, seq_len, head_dim] and [batch, kv_heads, nb] (transpose = 0).
+ * vt8, v_scale: [batch, kv_heads, head_dim, n_pad] and [batch, kv_heads, nb] (transpose = 1).
+ * o           : bf16 [batch, heads, seq_len, head_dim], written in full.
+ * lse         : optional fp32 [batch, heads, seq_len]: m + ln(l) of the rounded weights.
+ * seq_lens, kv_heads, causal, scale : as in attn_fwd (no window); the lengths must be the
+ *               ones the operands were quantised with.
+ * Supported   : head_dim 128.
+ */
+attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_scale,
+                         const float* k_scale, const float* v_scale, void* o, float* lse,
+                         const int32_t* seq_lens, int batch, int heads, int kv_heads,
+                         int seq_len, int head_dim, int causal, float scale, void* stream);
+
 /* attn_status_str — static, NUL-terminated name of a status code (never NULL). */
 const char* attn_status_str(attn_status status);
 

@@ -6,6 +6,8 @@ Entry points mirror the C ABI in include/attn.h:
     attn_bwd_workspace_bytes      workspace size the backward pass needs
     attn_decode_paged             one query per sequence against a paged bf16 K/V cache
     attn_decode_workspace_bytes   workspace size the decode needs
+    attn_quantize_fp8             bf16 -> FP8 E4M3 codes with one scale per 64-row block
+    attn_fwd_fp8                  prefill on E4M3 operands (bf16 output)
     attn_status_str, attn_abi_version
 """
 
@@ -20,6 +22,8 @@ from .binding import (
     attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_fwd,
+    attn_fwd_fp8,
+    attn_quantize_fp8,
     attn_status_str,
     lib,
 )
@@ -35,6 +39,8 @@ __all__ = [
     "attn_decode_paged",
     "attn_decode_workspace_bytes",
     "attn_fwd",
+    "attn_fwd_fp8",
+    "attn_quantize_fp8",
     "attn_status_str",
     "lib",
 ]

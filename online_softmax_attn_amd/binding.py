@@ -39,6 +39,9 @@ SIGNATURES = {
         [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
          _P, ctypes.c_size_t, _P],
     ),
+    "attn_quantize_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                          ctypes.c_float, _P]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
 }
@@ -266,4 +269,82 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len
         float(scale), int(kv_split), workspace.data_ptr(), ws_bytes, _stream(stream))
     if st != ATTN_OK:
         raise AttnError("attn_decode_paged", st)
+    return (out, lse) if return_lse else out
+
+
+# --------------------------------------------------------------------------- FP8 E4M3
+FP8_BLOCK = 64  # rows per quantisation block (one fp32 scale each)
+
+
+def attn_quantize_fp8(x, *, seq_lens=None, transpose=False, out=None, scales=None, stream=None):
+    """E4M3 codes (uint8) and fp32 block scales of a bf16 [B, H, n, 128] tensor.
+
+    transpose=False: codes [B, H, n, 128]; transpose=True: [B, H, 128, n_pad] with
+    n_pad = 64 * ceil(n / 64) (the V layout attn_fwd_fp8 reads).  scales: [B, H, ceil(n/64)].
+    Returns (codes, scales).
+    """
+    _check_dev("x", x, torch.bfloat16)
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, n, d]")
+    B, H, n, d = x.shape
+    nb = -(-n // FP8_BLOCK)
+    shape = (B, H, d, nb * FP8_BLOCK) if transpose else (B, H, n, d)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(B, H, nb, dtype=torch.float32, device=x.device)
+    _check_dev("out", out, torch.uint8)
+    _check_dev("scales", scales, torch.float32)
+    if tuple(out.shape) != shape or tuple(scales.shape) != (B, H, nb):
+        raise ValueError(f"out must be {shape} and scales {(B, H, nb)}")
+    lens = _lengths(seq_lens, B, n, x.device)
+    st = lib().attn_quantize_fp8(x.data_ptr(), out.data_ptr(), scales.data_ptr(),
+                                 lens.data_ptr() if lens is not None else None, B, H, n, d,
+                                 int(bool(transpose)), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError("attn_quantize_fp8", st)
+    return out, scales
+
+
+def attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, *, causal=False, scale=None,
+                 seq_lens=None, out=None, lse=None, return_lse=False, stream=None):
+    """Prefill attention on E4M3 operands from attn_quantize_fp8 (q, k row-major, v
+    transposed); bf16 output [B, H, n, 128]."""
+    for name, t in (("q8", q8), ("k8", k8), ("vt8", vt8)):
+        _check_dev(name, t, torch.uint8)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_dev(name, t, torch.float32)
+    if q8.dim() != 4 or k8.dim() != 4 or vt8.dim() != 4:
+        raise ValueError("q8, k8 must be [B, H, n, d]; vt8 [B, H_kv, d, n_pad]")
+    B, H, n, d = q8.shape
+    Hkv = int(k8.shape[1])
+    nb = -(-n // FP8_BLOCK)
+    if tuple(k8.shape) != (B, Hkv, n, d) or Hkv < 1 or H % Hkv:
+        raise ValueError("k8 must be [B, H_kv, n, d] with H a multiple of H_kv")
+    if tuple(vt8.shape) != (B, Hkv, d, nb * FP8_BLOCK):
+        raise ValueError("vt8 must be [B, H_kv, d, 64 * ceil(n / 64)]")
+    if (tuple(q_scale.shape) != (B, H, nb) or tuple(k_scale.shape) != (B, Hkv, nb)
+            or tuple(v_scale.shape) != (B, Hkv, nb)):
+        raise ValueError("scales must be [B, heads, ceil(n / 64)]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(B, H, n, d, dtype=torch.bfloat16, device=q8.device)
+    _check_dev("out", out, torch.bfloat16)
+    if tuple(out.shape) != (B, H, n, d):
+        raise ValueError("out must be [B, H, n, d]")
+    if lse is None and return_lse:
+        lse = torch.empty(B, H, n, dtype=torch.float32, device=q8.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if lse.shape != (B, H, n):
+            raise ValueError("lse must be [B, H, n]")
+    lens = _lengths(seq_lens, B, n, q8.device)
+    st = lib().attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_scale.data_ptr(),
+                            k_scale.data_ptr(), v_scale.data_ptr(), out.data_ptr(),
+                            lse.data_ptr() if lse is not None else None,
+                            lens.data_ptr() if lens is not None else None, B, H, Hkv, n, d,
+                            int(bool(causal)), float(scale), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError("attn_fwd_fp8", st)
     return (out, lse) if return_lse else out

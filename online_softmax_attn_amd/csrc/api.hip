@@ -103,6 +103,38 @@ attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void*
       reinterpret_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_quantize_fp8(const void* x, void* x8, float* scales, const int32_t* seq_lens,
+                              int batch, int heads, int seq_len, int head_dim, int transpose,
+                              void* stream) {
+  if (!x || !x8 || !scales) return ATTN_ERR_INVALID;
+  if (batch <= 0 || heads <= 0 || seq_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID;
+  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)batch * heads > 65535) return ATTN_ERR_UNSUPPORTED;  // grid.y limit
+  return launch_status(launch_quantize_fp8(static_cast<const bf16*>(x), static_cast<uint8_t*>(x8),
+                                           scales, seq_lens, batch, heads, seq_len, transpose != 0,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_scale,
+                         const float* k_scale, const float* v_scale, void* o, float* lse,
+                         const int32_t* seq_lens, int batch, int heads, int kv_heads,
+                         int seq_len, int head_dim, int causal, float scale, void* stream) {
+  if (!q8 || !k8 || !vt8 || !q_scale || !k_scale || !v_scale || !o) return ATTN_ERR_INVALID;
+  if (batch <= 0 || heads <= 0 || seq_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID;
+  if (!heads_window_ok(heads, kv_heads, 0)) return ATTN_ERR_INVALID;
+  if (!finite_positive(scale)) return ATTN_ERR_INVALID;
+  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  // 32-bit byte offsets inside one (batch, head) slice, also of the transposed V
+  const long long n_pad = (seq_len + 63LL) / 64 * 64;
+  if (n_pad * head_dim >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)batch * heads * ((seq_len + 127) / 128) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  return launch_status(launch_fwd_fp8(
+      static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
+      static_cast<const uint8_t*>(vt8), q_scale, k_scale, v_scale, static_cast<bf16*>(o), lse,
+      seq_lens, batch, heads, kv_heads, seq_len, causal != 0, scale,
+      reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t attn_decode_workspace_bytes(int batch, int heads, int kv_heads, int head_dim,
                                    int max_seq_len, int window, int kv_split) {
   if (batch <= 0 || heads <= 0 || head_dim != 128 || max_seq_len <= 0) return 0;

@@ -46,6 +46,14 @@ hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v
                                int max_blocks_per_seq, int max_seq_len, int window, float scale,
                                int split, void* workspace, hipStream_t stream);
 
+// FP8 E4M3 path: 64-row block quantisation, then attention on the codes.
+hipError_t launch_quantize_fp8(const bf16* x, uint8_t* x8, float* scales, const int32_t* seq_lens,
+                               int batch, int heads, int n, int transpose, hipStream_t stream);
+hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8,
+                          const float* q_scale, const float* k_scale, const float* v_scale,
+                          bf16* o, float* lse, const int32_t* seq_lens, int batch, int heads,
+                          int kv_heads, int n, int causal, float scale, hipStream_t stream);
+
 // ---------------------------------------------------------------------------------------
 // Buffer resources: loads through a buffer descriptor return 0 for any byte offset at or
 // past `bytes`, which is how out-of-range rows (ragged tails, padding) are zero-filled

@@ -103,13 +103,30 @@ def quantize_blocks(x, *, seq_lens=None, block: int = BLOCK):
     return vals, scales
 
 
+def _near_ties(P, tie_rel):
+    """E4M3 spacing at each weight that lies within tie_rel * p of a rounding midpoint (either
+    rounding is then a correct fp32 outcome), else 0."""
+    P = np.asarray(P, dtype=np.float64)
+    _, e = np.frexp(P)
+    q = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)
+    mid = (np.floor(P / q) + 0.5) * q
+    return np.where((P > 0) & (np.abs(P - mid) <= tie_rel * P), q, 0.0)
+
+
 def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, *, scale: float, causal: bool = False,
-                  seq_lens=None, block: int = BLOCK):
+                  seq_lens=None, block: int = BLOCK, tie_rel: float = 0.0):
     """The FP8 online-softmax loop over key tiles of `block` keys (rows in parallel).
 
     q8 [B, H, n, d], k8 / v8 [B, H_kv, n, d]: E4M3 values (float64); *_scale: fp32 block
     scales [B, heads, ceil(n / block)].  Returns (O float64 [B, H, n, d] before the output
     cast, LSE float64 [B, H, n]); rows with no admitted key give 0 / -inf.
+
+    The weights are rounded to E4M3 from fp32 values, and another correct fp32 evaluation
+    (a different summation order, exponential or scale folding) can land on the other side
+    of a rounding midpoint.  With tie_rel > 0 the function also returns (O_slack, LSE_slack):
+    for every weight within tie_rel * p of a midpoint, the largest change of the row's
+    output and LSE that rounding it the other way makes (first order, summed over such
+    weights).  Rows without near-ties have zero slack.
     """
     q8, k8, v8 = (np.asarray(a, dtype=np.float64) for a in (q8, k8, v8))
     B, H, n, d = q8.shape
@@ -117,6 +134,8 @@ def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, *, scale: float, causal
     lens = [n] * B if seq_lens is None else [int(v) for v in seq_lens]
     O = np.zeros((B, H, n, d))
     LSE = np.full((B, H, n), -math.inf)
+    O_slack = np.zeros((B, H, n, d))
+    LSE_slack = np.zeros((B, H, n))
     f32 = np.float32
     for b in range(B):
         L = lens[b]
@@ -129,6 +148,7 @@ def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, *, scale: float, causal
             m = np.full(L, -np.inf, dtype=f32)   # running maximum per row (fp32, natural units)
             l = np.zeros(L)
             u = np.zeros((L, d))
+            ties = []                           # (tile, spacing per weight, tile maximum)
             for t in range(-(-L // block)):
                 j0, j1 = t * block, min((t + 1) * block, L)
                 keys = np.arange(j0, j1)
@@ -146,6 +166,25 @@ def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, *, scale: float, causal
                 l = l * c + P8.sum(axis=1)
                 u = u * c[:, None] + float(v_scale[b, hk, t]) * (P8 @ v8[b, hk, j0:j1])
                 m = m_new
-            O[b, h, :L] = u / l[:, None]
+                if tie_rel > 0:
+                    ties.append((t, _near_ties(P.astype(f32), tie_rel), m_new.astype(np.float64)))
+            o = u / l[:, None]
+            O[b, h, :L] = o
             LSE[b, h, :L] = m.astype(np.float64) + np.log(l)
+            if tie_rel > 0:
+                mf = m.astype(np.float64)
+                dw_tot = np.zeros(L)
+                for t, sp, mt in ties:
+                    ri, kj = np.nonzero(sp)                       # the near-tie weights
+                    if len(ri) == 0:
+                        continue
+                    w = sp[ri, kj] * np.exp(mt[ri] - mf[ri])      # spacing at the row's end
+                    dv = float(v_scale[b, hk, t]) * v8[b, hk, t * block + kj]
+                    np.add.at(O_slack[b, h], ri, w[:, None] * np.abs(dv - o[ri]))
+                    np.add.at(dw_tot, ri, w)
+                denom = np.maximum(l - dw_tot, 1e-300)
+                O_slack[b, h, :L] /= denom[:, None]
+                LSE_slack[b, h, :L] = dw_tot / denom
+    if tie_rel > 0:
+        return O, LSE, O_slack, LSE_slack
     return O, LSE

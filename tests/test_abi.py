@@ -22,7 +22,7 @@ INVALID, UNSUPPORTED, WORKSPACE = (binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UN
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -140,3 +140,37 @@ def test_decode_workspace_bytes():
     assert f(2, 4, 128, 1000, 256, window=-1) == 0
     need = f(2, 4, 128, 128, 0, kv_heads=2, window=40)
     assert need > 0 and dec(Hkv=2, window=40, wsb=need - 1) == WORKSPACE
+
+
+def q8(**kw):
+    a = dict(x=FAKE, x8=FAKE, sc=FAKE, lens=None, B=1, H=2, n=100, d=128, tr=0)
+    a.update(kw)
+    return attn.lib().attn_quantize_fp8(a["x"], a["x8"], a["sc"], a["lens"], a["B"], a["H"], a["n"],
+                                        a["d"], a["tr"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(x8=None), INVALID), (dict(sc=None), INVALID),
+    (dict(B=0), INVALID), (dict(n=-1), INVALID), (dict(d=64), UNSUPPORTED),
+    (dict(B=300, H=300), UNSUPPORTED),
+])
+def test_quantize_fp8_validation(kw, status):
+    assert q8(**kw) == status
+
+
+def f8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sq=FAKE, sk=FAKE, sv=FAKE, o=FAKE, lse=None, lens=None, B=1,
+             H=4, Hkv=2, n=100, d=128, causal=1, scale=0.1)
+    a.update(kw)
+    return attn.lib().attn_fwd_fp8(a["q"], a["k"], a["v"], a["sq"], a["sk"], a["sv"], a["o"],
+                                   a["lse"], a["lens"], a["B"], a["H"], a["Hkv"], a["n"], a["d"],
+                                   a["causal"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(v=None), INVALID), (dict(sk=None), INVALID), (dict(o=None), INVALID),
+    (dict(H=0), INVALID), (dict(Hkv=3), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(n=1 << 24), UNSUPPORTED),
+])
+def test_fwd_fp8_validation(kw, status):
+    assert f8(**kw) == status

@@ -201,3 +201,30 @@ def test_grouped_heads_and_lengths():
                                   sq[:, h:h + 1], sk[:, h // 2:h // 2 + 1], sv[:, h // 2:h // 2 + 1],
                                   scale=0.3, causal=True, seq_lens=lens)
         np.testing.assert_array_equal(o1[:, 0], O[:, h])
+
+
+def test_near_tie_slack_covers_the_other_rounding():
+    """A weight placed next to the E4M3 midpoint 0.328125 (between 0.3125, mantissa even, and
+    0.34375): the loop rounds it to 0.3125; rounding it up instead gives
+    (v0 + 0.34375 v1) / 1.34375.  The reported slack must cover that difference, and rows
+    without a near-tie report none."""
+    scale = 0.5
+    x = math.log(0.328125) / scale
+    q = np.array([[[[1.0, 0.0], [1.0, 0.0]]]], np.float32)
+    k = np.array([[[[0.0, 0.0], [x, 0.0]]]], np.float32)
+    v = np.array([[[[1.0, 0.0], [0.0, 1.0]]]], np.float32)
+    q8, k8, v8, sq, sk, sv = quantized(q, k, v)
+    O, LSE, Os, Ls = fp8.attention_fp8(q8, k8, v8, sq, sk, sv, scale=scale, tie_rel=2.0 ** -16)
+    s_v = float(sv[0, 0, 0]) * 448
+    np.testing.assert_allclose(O[0, 0, 0], np.array([1.0, 0.3125]) / 1.3125 * s_v, rtol=1e-6)
+    alt = np.array([1.0, 0.34375]) / 1.34375 * s_v
+    diff = np.abs(alt - O[0, 0, 0])
+    assert np.all(diff <= Os[0, 0, 0]) and np.all(Os[0, 0, 0] <= 2 * diff + 1e-12), (diff, Os[0, 0, 0])
+    assert abs(math.log(1.34375) - LSE[0, 0, 0]) <= Ls[0, 0, 0]
+    # the same inputs with tie_rel 0: identical outputs; far from a tie: no slack
+    O2, L2 = fp8.attention_fp8(q8, k8, v8, sq, sk, sv, scale=scale)
+    np.testing.assert_array_equal(O, O2)
+    rng = np.random.default_rng(7)
+    qq, kk, vv = (rng.normal(size=(1, 1, 64, 8)).astype(np.float32) for _ in range(3))
+    _, _, Os3, Ls3 = fp8.attention_fp8(*quantized(qq, kk, vv), scale=0.3, tie_rel=1e-30)
+    assert np.all(Os3 == 0) and np.all(Ls3 == 0)
