@@ -30,6 +30,7 @@ constexpr int kBM = 128;    // queries per workgroup
 constexpr int kBN = 64;     // keys per tile (= the quantisation block)
 constexpr int kThreads = 256;
 constexpr int kTileBytes = kBN * kD;  // 8 KiB, for K and for V^T
+constexpr float kSlack = 8.0f;        // log2 headroom of the accumulation reference
 
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) uint4 lds_uint4;
@@ -132,12 +133,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     const int D = 2 * ln + (p >> 2);
     v_src[i] = D * (int)n_pad + 16 * ((p & 3) ^ (ln & 3));
   }
-  auto issue = [&](int t, int buf) {
+  auto issue_k = [&](int t, int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2; ++i)
       load_lds16(rk, (lds_void*)&Ks[buf][(2 * w + i) * 1024], t * kBN * kD + k_src[i]);
+  };
+  auto issue_v = [&](int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
       load_lds16(rv, (lds_void*)&Vs[buf][(2 * w + i) * 1024], t * kBN + v_src[i]);
-    }
   };
 
   floatx16 acc[4];  // O^T: lane holds d = 32 db + 8 (r/4) + 4 hl + r%4 of query qi
@@ -145,102 +149,145 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m_run = -INFINITY;  // running maximum of this lane's query, log2 units
-  float l_run = 0.f;
+  // m_cur: the exact running maximum (log2 units) through the last scored tile — the weights
+  // of a tile are taken against it.  m_ref: the reference acc and l_acc are kept in; it
+  // follows m_cur lazily (raised when m_cur exceeds it by more than kSlack), so a tile's
+  // contribution enters with the factor 2^(m_cur - m_ref) and the rescale of acc is rare.
+  float m_cur = -INFINITY, m_ref = -INFINITY, l_acc = 0.f;
   const intx8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
   const floatx16 zero16 = {};
 
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) issue(t + 1, buf ^ 1);
-    if (t < wave_tiles) {
-      const uint8_t* Kt = Ks[buf];
-      const uint8_t* Vt = Vs[buf];
-      const int k0 = t * kBN;
-      // ---- S^T = K Q^T: s[kb][r] is the raw score of key k0 + 32 kb + 16 hl + r
-      floatx16 s[2];
+  struct Tile {
+    floatx16 s[2];  // raw scores: s[kb][r] is key k0 + 32 kb + 16 hl + r (masked: -inf)
+  };
+  auto compute_s = [&](Tile& T, const uint8_t* Kt) {  // S^T = K Q^T, 4 MFMA
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) T.s[kb] = zero16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = zero16;
-        const int R = 32 * kb + lq;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int c0 = 4 * ks + 2 * hl;
-          const intx8 a = read32(Kt, k_off(R, c0), k_off(R, c0 + 1));
-          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qop[ks], s[kb], 0, 0, 0, 0, 0, 0);
-        }
+        const int R = 32 * kb + lq, c0 = 4 * ks + 2 * hl;
+        const intx8 a = read32(Kt, k_off(R, c0), k_off(R, c0 + 1));
+        T.s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qop[ks], T.s[kb], 0, 0, 0, 0, 0, 0);
       }
-      // ---- mask, tile maximum, exact running maximum
-      const float c = c_q * ks_row[t];  // scale * s_Q * s_K * log2(e)
-      const bool need_mask = (k0 + kBN > L) || (causal && k0 + kBN - 1 > wave_q_first);
-      float mx = -INFINITY;
+  };
+  auto need_mask = [&](int t) {
+    const int k0 = t * kBN;
+    return (k0 + kBN > L) || (causal && k0 + kBN - 1 > wave_q_first);
+  };
+  auto apply_mask = [&](Tile& T, int k0) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * c;
-          if (need_mask) {
-            const int key = k0 + 32 * kb + 16 * hl + r;
-            x = (key < L && (!causal || key <= qi)) ? x : -INFINITY;
-          }
-          s[kb][r] = x;
-          mx = __builtin_fmaxf(mx, x);
-        }
-      mx = other_half_max(mx);
-      const float m_new = __builtin_fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {
-        // floor at -1e30: a lane with no admitted key yet keeps alpha = 1 and weights 0
-        const float alpha = __builtin_amdgcn_exp2f(__builtin_fmaxf(m_run, -1e30f) - __builtin_fmaxf(m_new, -1e30f));
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * kb + 16 * hl + r;
+        T.s[kb][r] = (key < L && (!causal || key <= qi)) ? T.s[kb][r] : -INFINITY;
       }
-      m_run = m_new;
-      const float m_use = __builtin_fmaxf(m_new, -1e30f);
-      // ---- weights rounded to E4M3: byte e = 16 kb + r of the B operand
-      intx8 pop;
+  };
+  // tile maximum in log2 units; c > 0, so max(raw) * c is the max of the rounded products
+  auto row_max = [&](const Tile& T, float c) {
+    float mx = __builtin_fmaxf(T.s[0][0], T.s[0][1]);
 #pragma unroll
-      for (int wd = 0; wd < 8; ++wd) {
-        const int kb = wd >> 2, r0 = 4 * (wd & 3);
-        const float p0 = __builtin_amdgcn_exp2f(s[kb][r0] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(s[kb][r0 + 1] - m_use);
-        const float p2 = __builtin_amdgcn_exp2f(s[kb][r0 + 2] - m_use);
-        const float p3 = __builtin_amdgcn_exp2f(s[kb][r0 + 3] - m_use);
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        pop[wd] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
-      }
-      // ---- l += row sum of the rounded weights; O^T += s_V (V^T P^T)
-      const floatx16 lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pop, zero16, 0, 0, 0, 0, 0, 0);
-      const float sv = vs_row[t];
-      floatx16 tmp[4];
+    for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, T.s[0][r]), T.s[0][r + 1]);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int D = 32 * db + lq;
-        const intx8 a = read32(Vt, v_off(D, hl), v_off(D, 2 + hl));
-        tmp[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pop, zero16, 0, 0, 0, 0, 0, 0);
-      }
-      l_run += lsum[0];
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, T.s[1][r]), T.s[1][r + 1]);
+    return other_half_max(mx) * c;
+  };
+  auto weights = [&](const Tile& T, float c, float m_use, intx8& pop) {  // byte e = 16 kb + r
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) {
+      const int kb = wd >> 2, r0 = 4 * (wd & 3);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(T.s[kb][r0], c, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(T.s[kb][r0 + 1], c, -m_use));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(T.s[kb][r0 + 2], c, -m_use));
+      const float p3 = __builtin_amdgcn_exp2f(fmaf(T.s[kb][r0 + 3], c, -m_use));
+      const int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      pop[wd] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
+    }
+  };
+  auto raise_ref = [&]() {
+    if (__any(m_cur > m_ref + kSlack)) {
+      const float m_new = __builtin_fmaxf(__builtin_fmaxf(m_ref, m_cur), -1e30f);
+      const float alpha = __builtin_amdgcn_exp2f(__builtin_fmaxf(m_ref, -1e30f) - m_new);  // 0 from empty
+      m_ref = m_new;
+      l_acc *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] = fmaf(sv, tmp[db][r], acc[db][r]);
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
     }
-    __builtin_amdgcn_s_waitcnt(0);
+  };
+
+  // One pipelined step: the weights of tile t (in `cur`) are formed while the matrix cores
+  // compute the scores of tile t+1 (into `nxt`); then P(t) V(t) runs while the maximum of
+  // tile t+1 is taken and the previous products enter acc.  K loads run two tiles ahead,
+  // V loads one.
+  auto step = [&](int t, Tile& cur, Tile& nxt) {
+    if (t + 2 < n_tiles) issue_k(t + 2, t & 1);
+    if (t + 1 < n_tiles) issue_v(t + 1, (t + 1) & 1);
+    if (t < wave_tiles) {
+      const bool do_next = t + 1 < wave_tiles;
+      raise_ref();
+      const float m_use = __builtin_fmaxf(m_cur, -1e30f);
+      const float f = __builtin_amdgcn_exp2f(m_use - __builtin_fmaxf(m_ref, -1e30f));
+      intx8 pop;
+      if (do_next) compute_s(nxt, Ks[(t + 1) & 1]);
+      weights(cur, c_q * ks_row[t], m_use, pop);
+      // P.V in two halves of 64 dimensions (keeps 32 product registers live), the row sum
+      // of the rounded weights, and the next tile's mask and maximum in between
+      const float fv = f * vs_row[t];
+      floatx16 lsum;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        floatx16 tmp[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int D = 64 * half + 32 * i + lq;
+          const intx8 a = read32(Vs[t & 1], v_off(D, hl), v_off(D, 2 + hl));
+          tmp[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pop, zero16, 0, 0, 0, 0, 0, 0);
+        }
+        if (half == 0) {
+          lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pop, zero16, 0, 0, 0, 0, 0, 0);
+          if (do_next) {
+            if (need_mask(t + 1)) apply_mask(nxt, (t + 1) * kBN);
+            m_cur = __builtin_fmaxf(m_cur, row_max(nxt, c_q * ks_row[t + 1]));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[2 * half + i][r] = fmaf(tmp[i][r], fv, acc[2 * half + i][r]);
+      }
+      l_acc = fmaf(lsum[0], f, l_acc);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the next tiles has landed
     __syncthreads();
+  };
+
+  // ---- prologue: K(0), V(0), K(1) in flight; scores and maximum of tile 0
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (n_tiles > 1) issue_k(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  Tile ta, tb;
+  compute_s(ta, Ks[0]);
+  if (need_mask(0)) apply_mask(ta, 0);
+  m_cur = row_max(ta, c_q * ks_row[0]);
+  __syncthreads();  // every wave is done with K(0) before K(2) overwrites its buffer
+
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, ta, tb);
+    if (t + 1 < n_tiles) step(t + 1, tb, ta);
   }
 
   // ---- epilogue: o = u / l (l is the whole row's sum: every lane of the MFMA column has it)
   if (qi < n) {
     bf16* orow = O + o_base + (size_t)qi * kD;
     const bool valid = qi < L;
-    const float inv = 1.0f / l_run;
+    const float inv = 1.0f / l_acc;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -251,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * a + 4 * hl) = __builtin_convertvector(x, bf16x4);
       }
     if (LSE && hl == 0)
-      LSE[(size_t)bh * n + qi] = valid ? (m_run * ATTN_LN2 + __logf(l_run)) : -INFINITY;
+      LSE[(size_t)bh * n + qi] = valid ? (m_ref * ATTN_LN2 + __logf(l_acc)) : -INFINITY;
   }
 }
 

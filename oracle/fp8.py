@@ -103,30 +103,34 @@ def quantize_blocks(x, *, seq_lens=None, block: int = BLOCK):
     return vals, scales
 
 
-def _near_ties(P, tie_rel):
-    """E4M3 spacing at each weight that lies within tie_rel * p of a rounding midpoint (either
-    rounding is then a correct fp32 outcome), else 0."""
+def _near_ties(P, window):
+    """E4M3 spacing at each weight that lies within window * p of a rounding midpoint (either
+    rounding is then a correct outcome of an evaluation that precise), else 0."""
     P = np.asarray(P, dtype=np.float64)
     _, e = np.frexp(P)
     q = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)
     mid = (np.floor(P / q) + 0.5) * q
-    return np.where((P > 0) & (np.abs(P - mid) <= tie_rel * P), q, 0.0)
+    return np.where((P > 0) & (np.abs(P - mid) <= window * P), q, 0.0)
 
 
 def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, *, scale: float, causal: bool = False,
-                  seq_lens=None, block: int = BLOCK, tie_rel: float = 0.0):
+                  seq_lens=None, block: int = BLOCK, tie_rel: float = 0.0, acc_rel: float = 0.0):
     """The FP8 online-softmax loop over key tiles of `block` keys (rows in parallel).
 
     q8 [B, H, n, d], k8 / v8 [B, H_kv, n, d]: E4M3 values (float64); *_scale: fp32 block
     scales [B, heads, ceil(n / block)].  Returns (O float64 [B, H, n, d] before the output
     cast, LSE float64 [B, H, n]); rows with no admitted key give 0 / -inf.
 
-    The weights are rounded to E4M3 from fp32 values, and another correct fp32 evaluation
-    (a different summation order, exponential or scale folding) can land on the other side
-    of a rounding midpoint.  With tie_rel > 0 the function also returns (O_slack, LSE_slack):
-    for every weight within tie_rel * p of a midpoint, the largest change of the row's
-    output and LSE that rounding it the other way makes (first order, summed over such
-    weights).  Rows without near-ties have zero slack.
+    The weights are rounded to E4M3 from fp32 values, and another correct evaluation (a
+    different summation order, exponential or scale folding, or a product unit that sums
+    its terms with less than fp32 precision) can land on the other side of a rounding
+    midpoint.  With tie_rel > 0 the function also returns (O_slack, LSE_slack): for every
+    weight within `window` * p of a midpoint, the largest change of the row's output and LSE
+    that rounding it the other way makes (first order, summed over such weights); rows
+    without near-ties have zero slack.  window = tie_rel + 2 * acc_rel * alpha * 2 * 448^2:
+    acc_rel bounds the error of one 64-term block of the score sum relative to its largest
+    term (at most 448^2 in code units; two blocks per 128-dim score, alpha = scale s_Q s_K
+    converts to score units, and a weight exp(S - m) moves by the error of S and of m).
     """
     q8, k8, v8 = (np.asarray(a, dtype=np.float64) for a in (q8, k8, v8))
     B, H, n, d = q8.shape
@@ -167,7 +171,8 @@ def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, *, scale: float, causal
                 u = u * c[:, None] + float(v_scale[b, hk, t]) * (P8 @ v8[b, hk, j0:j1])
                 m = m_new
                 if tie_rel > 0:
-                    ties.append((t, _near_ties(P.astype(f32), tie_rel), m_new.astype(np.float64)))
+                    window = tie_rel + 2 * acc_rel * alpha.astype(np.float64) * 2 * E4M3_MAX ** 2
+                    ties.append((t, _near_ties(P.astype(f32), window[:, None]), m_new.astype(np.float64)))
             o = u / l[:, None]
             O[b, h, :L] = o
             LSE[b, h, :L] = m.astype(np.float64) + np.log(l)

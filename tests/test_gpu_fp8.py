@@ -2,17 +2,20 @@
 
 The quantisation is integer work: codes and scales must match the oracle bit for bit (both
 divide in fp32 and round to nearest even).  The attention then runs on identical E4M3
-operands, so the GPU and the oracle's tiled FP8 loop differ only by fp32 rounding of the
-scores and exponentials; the bf16 tolerances apply (max-abs 1e-2, mean-abs 1e-3, LSE 2^-8)
-against the oracle's output rounded to the output format (bf16, nearest even): unlike the
-bf16 path, a dequantised value s_V * v8 is in general not a bf16 number, so the output's own
-rounding (mean 2^-9 |o|) would otherwise use up the mean tolerance on short rows.
-A rounding decision of a weight can still flip where the two fp32 evaluations straddle an
-E4M3 midpoint; both roundings are then correct outcomes of the method.  The oracle reports,
-per output element, the largest change such near-ties (weights within 2^-16 p of a
-midpoint, far beyond the few-ulp differences of two fp32 evaluations) can make, and the
-max-abs and LSE bounds are widened by exactly that slack; rows without near-ties keep the
-plain bounds."""
+operands; the GPU and the oracle's tiled FP8 loop differ by the precision of the score
+sums and exponentials.  Element-wise the GPU output must lie within half a bf16 ulp of the
+oracle's value (its own output rounding: a dequantised s_V * v8 is in general not a bf16
+number) plus 2^-10; mean-abs against the oracle rounded to bf16 within 1e-3; LSE within
+2^-8.
+
+A weight's E4M3 rounding can flip where the two evaluations straddle a rounding midpoint;
+both roundings are then correct outcomes of the method.  The oracle reports, per output
+element, the largest change such near-ties can make, and the element-wise and LSE bounds
+are widened by exactly that slack (rows without near-ties keep the plain bounds).  The
+near-tie window is 2^-16 p for fp32 differences (exponential, scale folding) plus the
+matrix cores' accumulation error: the fp8 MFMA does not sum its 64 products with full fp32
+precision (measured against exact sums: up to 2^-12.9 of the largest product, median
+2^-16), so 2^-12 of the largest possible product per 64-term block is allowed."""
 
 import math
 
@@ -31,6 +34,10 @@ pytestmark = pytest.mark.gpu
 BF16_MAX, BF16_MEAN = 1e-2, 1e-3
 LSE_ATOL = 2.0 ** -8
 TIE_REL = 2.0 ** -16
+# v_mfma_f32_32x32x64_f8f6f4 does not sum its 64 products with full fp32 precision: measured
+# on random block-quantised operands, the error against the exact sum reaches 2^-12.9 of the
+# largest product (median 2^-16); the near-tie window allows 2^-12 per 64-term block.
+ACC_REL = 2.0 ** -12
 
 
 def oracle_quantized(q, k, v, lens):
@@ -77,20 +84,25 @@ def oracle_fp8(q, k, v, *, causal, lens, heads=None):
         q8, sq = q8[:, heads], sq[:, heads]
         k8, sk, v8, sv = k8[:, kv], sk[:, kv], v8[:, kv], sv[:, kv]
     return fp8.attention_fp8(q8, k8, v8, sq, sk, sv, scale=float(np.float32(1 / math.sqrt(128))),
-                             causal=causal, seq_lens=lens, tie_rel=TIE_REL)
+                             causal=causal, seq_lens=lens, tie_rel=TIE_REL, acc_rel=ACC_REL)
 
 
 def check(o, lse, ref, rows=None):
-    """max-abs and LSE bounds widened by the near-tie slack; plain mean-abs bound."""
+    """Element-wise: |o - ref| within the output's own bf16 rounding (half an ulp at ref),
+    the near-tie slack, and 2^-10 for fp32 evaluation differences; mean-abs against the
+    bf16-rounded reference within 1e-3; LSE within 2^-8 plus its slack."""
     ro, rl, o_slack, l_slack = ref
     if rows is None:
         rows = np.ones(o.shape[:3], dtype=bool)
-    err = np.abs(o - as_bf16(ro))[rows]
-    excess = np.maximum(err - o_slack[rows], 0.0)
+    err = np.abs(o - ro)[rows]
+    mag = np.abs(ro[rows])
+    half_ulp = np.where(mag > 0, np.ldexp(1.0, np.frexp(mag)[1] - 9), 0.0)
+    excess = np.maximum(err - half_ulp - o_slack[rows], 0.0)
+    mean = np.abs(o - as_bf16(ro))[rows].mean()
     flips = int((o_slack[rows].max(axis=-1) > 0).sum())
-    print(f"max-abs {err.max():.5f} (beyond tie slack {excess.max():.5f}, {flips} rows with "
-          f"near-ties) mean-abs {err.mean():.2e}")
-    assert excess.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (excess.max(), err.mean())
+    print(f"max-abs {err.max():.5f}, beyond bf16 rounding and tie slack {excess.max():.2e} "
+          f"({flips} rows with near-ties); mean-abs vs bf16(ref) {mean:.2e}")
+    assert excess.max() <= 2.0 ** -10 and mean <= BF16_MEAN, (excess.max(), mean)
     assert np.all(np.abs(lse[rows] - rl[rows]) <= LSE_ATOL + l_slack[rows])
 
 
