@@ -168,8 +168,8 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_cac
 
 /*
  * attn_quantize_fp8 — block quantisation of a bf16 tensor to FP8 E4M3, the operand format of
- * attn_fwd_fp8.  The FP8 section of the aimpact.prandi.net FlashAttention page
- * ("Quantizzazione a Blocchi e Scaling Algebrico") gives each block X the scale
+ * attn_fwd_fp8.  The FP8 part of pierluigilucio.it "Sviluppo AI ed Algebra Lineare" (section
+ * "Quantizzazione a Blocchi e Scaling Algebrico") gives each block X the scale
  * s = max|X| / 448 and the codes clip(round(X / s), -448, 448); here a block is 64 rows of
  * one (batch, head), X / s is a correctly rounded fp32 division, and rounding is to nearest,
  * ties to even.  A block that is all 0 gets s = 0 and codes 0.
@@ -188,8 +188,8 @@ attn_status attn_quantize_fp8(const void* x, void* x8, float* scales, const int3
                               void* stream);
 
 /*
- * attn_fwd_fp8 — prefill attention on E4M3 operands with per-block scales (FP8 section of the
- * aimpact.prandi.net FlashAttention page): scores (scale * s_Q * s_K) * (Q8 K8^T) accumulated
+ * attn_fwd_fp8 — prefill attention on E4M3 operands with per-block scales (pierluigilucio.it
+ * "Sviluppo AI ed Algebra Lineare", FP8 part, "Integrazione nel ciclo Online Softmax"): scores (scale * s_Q * s_K) * (Q8 K8^T) accumulated
  * in fp32; maximum, differences and exponentials in fp32; the weights rounded to E4M3 before
  * the P.V product (fp32 accumulation); l sums the rounded weights; o = u / l cast to bf16.
  * The running maximum moves once per 64-key tile (the quantisation block), exactly.

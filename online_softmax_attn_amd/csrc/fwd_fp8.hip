@@ -1,7 +1,8 @@
 // FP8 (E4M3) prefill attention on gfx950 matrix cores, head_dim 128, bf16 output.
 //
-// The FP8 variant of the aimpact.prandi.net FlashAttention page (FP8 section of
-// FlashAttention-3): Q, K, V arrive as E4M3 codes with one fp32 scale per 64-row block
+// The FP8 variant of pierluigilucio.it "Sviluppo AI ed Algebra Lineare" (its part on FP8 in
+// FlashAttention-3, sections "Quantizzazione a Blocchi e Scaling Algebrico" and
+// "Integrazione nel ciclo Online Softmax"): Q, K, V arrive as E4M3 codes with one fp32 scale per 64-row block
 // (s = max|X| / 448, produced by quantize_fp8_kernel); the score block is
 // (scale s_Q s_K) (Q8 K8^T), the factor applied once in fp32 to the fp32 accumulator; the
 // maximum, S - m and exp(S - m) are fp32; the weights are rounded to E4M3 (v_cvt_pk_fp8_f32)

@@ -1,7 +1,7 @@
 // Block quantisation of bf16 [B, H, n, 128] tensors to FP8 E4M3 on gfx950.
 //
-// aimpact.prandi.net FlashAttention page, FP8 section ("Quantizzazione a Blocchi e Scaling
-// Algebrico"): a block X of rows gets the scale s = max|X| / 448 (448 = the largest E4M3
+// pierluigilucio.it "Sviluppo AI ed Algebra Lineare", FP8 part on FlashAttention-3, section
+// "Quantizzazione a Blocchi e Scaling Algebrico": a block X of rows gets the scale s = max|X| / 448 (448 = the largest E4M3
 // magnitude) and the codes clip(round(X / s), -448, 448).  Blocks are 64 rows of one
 // (batch, head); rows at or past the sequence length count as 0 and are written as code 0;
 // a block with max|X| = 0 has s = 0 and codes 0.  X / s is a correctly rounded fp32

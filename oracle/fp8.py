@@ -1,7 +1,7 @@
 """FP8 (E4M3) block-scaled attention, step by step — TEST INFRASTRUCTURE.
 
-Source: aimpact.prandi.net FlashAttention page, section on FP8 quantisation and mixed-
-precision accumulation in FlashAttention-3:
+Source: pierluigilucio.it "Sviluppo AI ed Algebra Lineare", the part on FP8 quantisation and
+mixed-precision accumulation in FlashAttention-3:
   * format: E4M3 = 1 sign bit, 4 exponent bits, 3 mantissa bits, largest magnitude 448
     (section "I Due Formati FP8").  The exponent bias (7), the subnormals (m * 2^-9) and the
     absence of infinities are the OCP "E4M3FN" definition the page names; rounding is to
