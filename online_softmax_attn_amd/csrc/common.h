@@ -46,6 +46,14 @@ hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v
                                int max_blocks_per_seq, int max_seq_len, int window, float scale,
                                int split, void* workspace, hipStream_t stream);
 
+// Grouped-head decode on the matrix cores (partials in the layout decode_merge_kernel reads);
+// launch_decode_paged picks it for groups of 8 or more query heads per K/V head.
+hipError_t launch_decode_gqa(const bf16* q, const bf16* k_cache, const bf16* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, int batch,
+                             int heads, int kv_heads, int num_blocks, int max_blocks_per_seq,
+                             int max_seq_len, int window, float scale, int split, int max_splits,
+                             void* workspace, size_t n_part, hipStream_t stream);
+
 // FP8 E4M3 path: 64-row block quantisation, then attention on the codes.
 hipError_t launch_quantize_fp8(const bf16* x, uint8_t* x8, float* scales, const int32_t* seq_lens,
                                int batch, int heads, int n, int transpose, hipStream_t stream);

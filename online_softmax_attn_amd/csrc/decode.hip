@@ -292,10 +292,25 @@ int max_splits_for(int max_seq_len, int window, int split) {
   return (span_blocks(max_seq_len, window) + split_blocks - 1) / split_blocks;
 }
 
-// Query heads one wave serves: the largest of 8, 4, 2, 1 that divides the group size.
+// Groups of at least this many query heads per K/V head run on the matrix cores
+// (decode_gqa_kernel); smaller ones on the vector units (decode_split_kernel).  Measured on
+// 32 sequences of 1024..8192 tokens, 8 K/V heads: the vector kernel reads 4.0 / 2.3 / 1.2 TB/s
+// at 4 / 8 / 16 heads per group (its work per byte grows with the group), the matrix-core
+// kernel 3.0 TB/s at every group size.
+constexpr int kMfmaGroup = 8;
+
+// Query heads one wave of decode_split_kernel serves: the largest of 8, 4, 2, 1 that divides
+// the group size.
 int heads_per_wave(int heads, int kv_heads) {
   const int G = heads / kv_heads;
   return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+}
+
+// waves per (sequence, split): decode_gqa_kernel takes up to 32 heads of a group per wave
+long long waves_per_split(int heads, int kv_heads) {
+  const int G = heads / kv_heads;
+  if (G >= kMfmaGroup) return (long long)kv_heads * ((G + 31) / 32);
+  return heads / heads_per_wave(heads, kv_heads);
 }
 
 }  // namespace
@@ -306,7 +321,7 @@ int heads_per_wave(int heads, int kv_heads) {
 // 512: 376 us, 768: 376 us, 1024: 378 us.
 int decode_default_split(int batch, int heads, int kv_heads, int max_seq_len, int window) {
   constexpr long long kTargetWaves = 8192;
-  const long long wave_heads = (long long)heads / heads_per_wave(heads, kv_heads);
+  const long long wave_heads = waves_per_split(heads, kv_heads);
   const long long span = (long long)span_blocks(max_seq_len, window) * kBlock;
   for (int split : {512, 256, 128}) {
     const long long waves = (long long)batch * wave_heads * ((span + split - 1) / split);
@@ -328,6 +343,17 @@ hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v
                                int split, void* workspace, hipStream_t stream) {
   const int max_splits = max_splits_for(max_seq_len, window, split);
   const size_t n_part = (size_t)batch * heads * max_splits;
+  if (heads / kv_heads >= kMfmaGroup) {
+    const hipError_t e = launch_decode_gqa(q, k_cache, v_cache, block_table, seq_lens, batch, heads,
+                                           kv_heads, num_blocks, max_blocks_per_seq, max_seq_len,
+                                           window, scale, split, max_splits, workspace, n_part,
+                                           stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(heads, batch), dim3(64), 0, stream, workspace,
+                       seq_lens, o, lse, heads, max_seq_len, window, max_splits, split / kBlock,
+                       n_part);
+    return hipGetLastError();
+  }
   const int gq = heads_per_wave(heads, kv_heads);
   const dim3 grid((unsigned)(heads / gq), (unsigned)max_splits, (unsigned)batch);
   const float c_log2 = scale * ATTN_LOG2E;
