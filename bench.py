@@ -3,8 +3,13 @@
 One step = one causal bf16 prefill over the [4, 32, 2048, 128] workload (attn_fwd) plus one
 paged decode of 32 sequences x 32 heads, d = 128, KV lengths U{1024..8192} in 16-token
 pages (attn_decode_paged).  Inputs are generated on the host from fixed seeds and moved to
-HBM before timing.  W warm-up steps, then K timed steps bracketed by synchronisations;
-each kernel call is also bracketed by HIP events on the stream it is launched on.
+HBM before timing.  W warm-up steps, then K timed steps bracketed by synchronisations, run
+as two back-to-back bursts (K prefills, then K decodes), each bracketed by HIP events on the
+stream the kernels are launched on (an event between two kernels would add the next one's
+dispatch latency to every launch).  The prefills run back to back on one input set (their
+201 MB of inputs stay in the 256 MB MALL, as after the projection that writes them); the
+same prefill with cold caches (launches cycling over 600 MB of input copies) is reported
+beside it.
 
 Prints ONE JSON line.  `value` is the prefill throughput in algorithmic TFLOP/s (only the
 admitted causal pairs, QK^T and PV: 4 d B H n(n+1)/2 flops); the decode throughput in
@@ -25,9 +30,9 @@ oracle timed on this host over a bounded sample of the prefill workload.
                   [1, 32, 16384, 128] (flops of the admitted pairs only) and the decode
                   workload reading each sequence's last 1024 tokens.
 --workload fp8    the causal prefill [4, 32, 2048, 128] on FP8 E4M3 operands (attn_fwd_fp8), the
-                  block quantisation of Q, K, V (attn_quantize_fp8) timed apart; a 512 MiB
-                  write between steps keeps the caches cold; the roofline is the dense fp8
-                  MFMA peak.
+                  block quantisation of Q, K, V (attn_quantize_fp8) timed apart; timed and
+                  reported like the bf16 prefill (warm, plus a cold reference); the
+                  roofline is the dense fp8 MFMA peak.
 --profile-pass    runs one 1 GiB device copy, one prefill and one decode and exits (the
                   command the rocprofv3 counter and trace runs wrap).
 --record-traffic FETCH_CSV WRITE_CSV
@@ -187,15 +192,16 @@ def bench_backward(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     t0 = time.perf_counter()
-    for e in ev:
-        e[0].record()
+    step()  # untimed: keeps the GPU busy while the event and the burst are enqueued
+    ev[0].record()
+    for _ in range(args.steps):
         step()
-        e[1].record()
+    ev[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
     flops = 2.5 * causal_flops(B, H, n, d)
     tf = flops / (ms * 1e-3) / 1e12
     print(json.dumps({
@@ -225,16 +231,19 @@ def bench_fp8(args):
         return (attn.attn_quantize_fp8(q), attn.attn_quantize_fp8(k),
                 attn.attn_quantize_fp8(v, transpose=True))
 
-    (q8, sq), (k8, sk), (v8, sv) = quantize()
+    one = quantize()
+    set_bytes = sum(x.numel() * x.element_size() for x in (one[0][0], one[1][0], one[2][0]))
+    n_sets = max(1, -(-(600 << 20) // set_bytes))
+    sets = [one] + [tuple((a.clone(), b.clone()) for a, b in one) for _ in range(n_sets - 1)]
     o = torch.empty(B, H, n, d, dtype=torch.bfloat16, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
-    def step():
+    def step(i=0):
+        (q8, sq), (k8, sk), (v8, sv) = sets[i % n_sets]
         attn.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=True, out=o)
 
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
         quantize()
-        step()
+        step(i)
     torch.cuda.synchronize()
     # quantisation of Q, K, V (a separate op: the attention's inputs are FP8 in HBM)
     qe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -244,18 +253,26 @@ def bench_fp8(args):
     qe[1].record()
     torch.cuda.synchronize()
     q_ms = qe[0].elapsed_time(qe[1]) / args.steps
-    # attention steps; 512 MiB written between steps (untimed) so no step finds its operands
-    # in the caches left by the previous one, as in the bf16 bench step after a decode
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # attention: K launches back to back on one input set (warm, as the bf16 prefill), one
+    # event pair around them; then a cold reference cycling over the input copies
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     t0 = time.perf_counter()
-    for e in ev:
-        flush.fill_(1)
-        e[0].record()
-        step()
-        e[1].record()
+    step(0)  # untimed: keeps the GPU busy while the event and the burst are enqueued
+    ev[0].record()
+    for _ in range(args.steps):
+        step(0)
+    ev[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    cold = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    step(n_sets - 1)
+    cold[0].record()
+    for i in range(args.steps):
+        step(i)
+    cold[1].record()
+    torch.cuda.synchronize()
+    cold_ms = cold[0].elapsed_time(cold[1]) / args.steps
     flops = causal_flops(B, H, n, d)
     tf = flops / (ms * 1e-3) / 1e12
     print(json.dumps({
@@ -267,7 +284,9 @@ def bench_fp8(args):
         "config": {"workload": "causal prefill B=4 H=32 n=2048 d=128, E4M3 operands, bf16 output"},
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
-        "ms_avg": round(ms, 5), "quantize_ms_avg": round(q_ms, 5)}))
+        "ms_avg": round(ms, 5), "cold_ms_avg": round(cold_ms, 5),
+        "cold_tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2), "cold_input_sets": n_sets,
+        "quantize_ms_avg": round(q_ms, 5)}))
 
 
 def main():
@@ -347,8 +366,15 @@ def main():
         dbytes = decode_bytes(pw, kv_heads, 128, window)
         dec = (dq, kc, vc, tbl, lens, do, ws, pw.max_seq_len)
 
-    def prefill():
-        attn.attn_fwd(q, k, v, causal=True, window=window, out=o)
+    # Prefill inputs cycle over enough copies that a launch never finds its Q/K/V in the
+    # 256 MB MALL left by the previous one (the copies together exceed 600 MB).
+    set_bytes = 3 * q.numel() * q.element_size()
+    n_sets = max(1, -(-(600 << 20) // set_bytes))
+    sets = [(q, k, v)] + [(q.clone(), k.clone(), v.clone()) for _ in range(n_sets - 1)]
+
+    def prefill(i=0):
+        qq, kk, vv = sets[i % n_sets]
+        attn.attn_fwd(qq, kk, vv, causal=True, window=window, out=o)
 
     def decode():
         dq, kc, vc, tbl, lens, do, ws, msl = dec
@@ -366,28 +392,46 @@ def main():
         print(json.dumps({"profile_pass": True, "copy_bytes": 1 << 30, "workload": args.workload}))
         return
 
-    for _ in range(args.warmup):
-        prefill()
+    for i in range(args.warmup):
+        prefill(i)
         if dec:
             decode()
     torch.cuda.synchronize()
 
+    # The K steps run as two back-to-back bursts, K prefills then K decodes, each bracketed by
+    # events on the launch stream: an event between two kernels would add the next kernel's
+    # dispatch latency (~10 us) to every measured launch.  The prefills run on one input set,
+    # back to back, as a prefill reads Q/K/V its producer has just written (warm in the
+    # 256 MB MALL); the decode's 2.3 GB cache is far larger than the MALL, so it reads HBM.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record()
-        prefill()
-        ev[i][1].record()
-        if dec:
+    # one untimed launch keeps the GPU busy while the first event and the burst are enqueued,
+    # so the first measured launch starts right behind the event, not one host round later
+    prefill(0)
+    ev[0].record()
+    for _ in range(K):
+        prefill(0)
+    ev[1].record()
+    if dec:
+        for _ in range(K):
             decode()
-        ev[i][2].record()
+    ev[2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the same prefill with cold caches, for reference: launches cycle over input copies
+    # (600 MB together), so none finds its Q/K/V in the MALL
+    cold = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    prefill(n_sets - 1)
+    cold[0].record()
+    for i in range(K):
+        prefill(i)
+    cold[1].record()
+    torch.cuda.synchronize()
+    cold_avg = cold[0].elapsed_time(cold[1]) / K
 
-    pre_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
-    pre_avg = sum(pre_ms) / K
+    pre_avg = ev[0].elapsed_time(ev[1]) / K
     achieved = flops / (pre_avg * 1e-3) / 1e12
     traffic = recorded_traffic("prefill") if args.workload == "prefill" else None
     result = {
@@ -406,19 +450,20 @@ def main():
         "config": {"workload": pre_cfg + (dec_cfg if dec else ""),
                    "batch": B, "heads": H, "kv_heads": kv_heads, "seq_len": n, "head_dim": d,
                    "causal": True, "window": window},
-        "prefill": {"ms_avg": round(pre_avg, 5), "ms_min": round(min(pre_ms), 5),
-                    "tflops": round(achieved, 2), "frac_of_peak": round(achieved / PEAK_BF16_TFLOPS, 4)},
+        "prefill": {"ms_avg": round(pre_avg, 5), "tflops": round(achieved, 2),
+                    "frac_of_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "cold_ms_avg": round(cold_avg, 5),
+                    "cold_tflops": round(flops / (cold_avg * 1e-3) / 1e12, 2),
+                    "cold_input_sets": n_sets},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
     if dec:
-        dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
-        dec_avg = sum(dec_ms) / K
+        dec_avg = ev[1].elapsed_time(ev[2]) / K
         gbs = dbytes / (dec_avg * 1e-3) / 1e9
         result["decode"] = {
-            "value": round(gbs, 1), "unit": "GB/s", "ms_avg": round(dec_avg, 5),
-            "ms_min": round(min(dec_ms), 5), "bytes": dbytes,
+            "value": round(gbs, 1), "unit": "GB/s", "ms_avg": round(dec_avg, 5), "bytes": dbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": recorded_traffic("decode") if args.workload == "prefill" else None},
