@@ -140,7 +140,8 @@ def check_decode_lse(lse, rl, group):
         np.testing.assert_allclose(lse, rl, rtol=2e-6, atol=2e-5)
 
 
-# (lens, H, H_kv, window, split): group sizes 1, 2, 3, 4, 8 and 16 (served 8 at a time)
+# (lens, H, H_kv, window, split): group sizes 1, 2, 3 and 4 (vector kernel), 8 and 16
+# (matrix-core kernel)
 DECODE_CASES = [
     ([1, 15, 16, 17], 8, 2, 0, 16), ([33, 250, 256, 257], 8, 8, 20, 32),
     ([1000, 3, 700], 16, 2, 0, 0), ([1000, 3, 700], 16, 2, 100, 0),
