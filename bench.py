@@ -3,13 +3,13 @@
 One step = one causal bf16 prefill over the [4, 32, 2048, 128] workload (attn_fwd) plus one
 paged decode of 32 sequences x 32 heads, d = 128, KV lengths U{1024..8192} in 16-token
 pages (attn_decode_paged).  Inputs are generated on the host from fixed seeds and moved to
-HBM before timing.  W warm-up steps, then K timed steps bracketed by synchronisations, run
-as two back-to-back bursts (K prefills, then K decodes), each bracketed by HIP events on the
-stream the kernels are launched on (an event between two kernels would add the next one's
-dispatch latency to every launch).  The prefills run back to back on one input set (their
-201 MB of inputs stay in the 256 MB MALL, as after the projection that writes them); the
-same prefill with cold caches (launches cycling over 600 MB of input copies) is reported
-beside it.
+HBM before timing.  W warm-up steps (enough for the shader clock to settle), then K timed
+steps bracketed by synchronisations, run as two back-to-back bursts (K prefills, then K
+decodes), each bracketed by HIP events on the stream the kernels are launched on (an event
+between two kernels would add the next one's dispatch latency to every launch).  The
+prefills run back to back on one input set (their 201 MB of inputs stay in the 256 MB MALL,
+as after the projection that writes them); the same prefill with cold caches (launches
+cycling over 600 MB of input copies) is reported beside it.
 
 Prints ONE JSON line.  `value` is the prefill throughput in algorithmic TFLOP/s (only the
 admitted causal pairs, QK^T and PV: 4 d B H n(n+1)/2 flops); the decode throughput in
@@ -296,7 +296,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The shader clock ramps up over the first ~20 ms of sustained work (a burst of prefills
+    # right after 5 warm-up steps runs ~15% slower than the same burst 30 ms later), so the
+    # default warm-up keeps the GPU busy for ~60 ms before anything is timed.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", choices=["prefill", "long", "backward", "grouped", "window", "fp8"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
