@@ -18,10 +18,13 @@
 //     bf16 weights P^T feed the MFMA B operand straight from the score registers; V^T is
 //     read from a row-major V tile with ds_read_b64_tr_b16, whose 16-lane transpose hands
 //     each lane 4 consecutive keys of one dimension.
-//   * K/V tiles (64 x 128 bf16 = 16 KiB each) are double-buffered in LDS: the next tile is
-//     fetched into registers with 128-bit loads while the current one is consumed, then
-//     stored with an XOR swizzle that keeps both the K row reads and the transposed V
-//     reads free of bank conflicts.  One barrier per tile.
+//   * K/V tiles (64 x 128 bf16 = 16 KiB each) are double-buffered in LDS and filled by
+//     16-byte-per-lane buffer loads that write LDS directly (no register staging), each lane
+//     fetching the chunk an XOR swizzle puts in its slot; the swizzle keeps both the K row
+//     reads and the transposed V reads free of bank conflicts.  K runs two tiles ahead of
+//     its use, V one.  One barrier per tile.
+//   * the output tile is staged through the then idle K buffers so that every store writes
+//     four whole 256-byte rows.
 //   * exp is v_exp_f32 (2^x): scores are scaled by scale*log2(e) inside one FMA.
 //   * the normaliser sums the bf16-ROUNDED weights that enter the P.V product (dot2 with
 //     ones), so rounding of P cancels in u/l to first order.
@@ -332,25 +335,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     if (t + 1 < n_tiles) step(t + 1, tb, ta);
   }
 
-  // ---- epilogue: o = u / l
+  // ---- epilogue: o = u / l, staged through LDS so that each store instruction writes four
+  // whole 256-byte rows of O.  Every wave has passed the last step's barrier, so the K
+  // buffers are free: wave w takes 8 KiB of them, its 32 rows with the 16-byte chunks of row
+  // r XOR-swizzled by r % 16.
   const float l_tot = other_half_sum(l_run);
-  if (qi < n) {
-    bf16* orow = O + base + (size_t)qi * kD;
-    const bool valid = qi < L;
-    const float inv = 1.0f / l_tot;
+  const bool valid = qi < L;
+  const float inv = 1.0f / l_tot;
+  bf16* stage = &Ks[0][0] + w * (32 * kD);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        floatx4 x;
+    for (int a = 0; a < 4; ++a) {
+      floatx4 x;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) x[c] = valid ? acc[db][4 * a + c] * inv : 0.f;
-        const bf16x4 y = __builtin_convertvector(x, bf16x4);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * a + 4 * hl) = y;
-      }
-    if (LSE && hl == 0)
-      LSE[(size_t)bh * n + qi] = valid ? (m_ref * ATTN_LN2 + __logf(l_tot)) : -INFINITY;
+      for (int c = 0; c < 4; ++c) x[c] = valid ? acc[db][4 * a + c] * inv : 0.f;
+      const int chunk = (4 * db + a) ^ (lq & 15);
+      *reinterpret_cast<bf16x4*>(stage + lq * kD + 8 * chunk + 4 * hl) =
+          __builtin_convertvector(x, bf16x4);
+    }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 4 * j + (lane >> 4), c = lane & 15;
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(stage + r * kD + 8 * (c ^ (r & 15)));
+    const int row = m0 + w * 32 + r;
+    if (row < n) *reinterpret_cast<bf16x8*>(O + base + (size_t)row * kD + 8 * c) = y;
   }
+  if (LSE && hl == 0 && qi < n)
+    LSE[(size_t)bh * n + qi] = valid ? (m_ref * ATTN_LN2 + __logf(l_tot)) : -INFINITY;
 }
 
 }  // namespace
