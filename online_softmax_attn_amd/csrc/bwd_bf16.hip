@@ -11,12 +11,13 @@
 //     dS_ij = P_ij (dP_ij - D_i)        dQ_i = scale sum_j dS_ij k_j
 //                                       dK_j = scale sum_i dS_ij q_i
 // Three kernels: D (a row reduction), dQ (one wave per 32 queries, sweeping key tiles, as
-// the forward pass does) and dK/dV (one wave per 32 keys, sweeping query tiles).  Both
-// sweeps use the forward's register layouts: the MFMA column is the row that owns the
-// accumulator (a query for dQ, a key for dK/dV), weights go from the score registers to
-// the B operand as bf16, and the transposed A operands (K^T for dQ; dO^T and Q^T for dK/dV)
-// come from row-major LDS tiles through ds_read_b64_tr_b16.  Masked pairs get weight 0 by
-// selection, so padding never enters a sum whatever it holds.
+// the forward pass does) and dK/dV (a pair of waves per 32 keys, sweeping query tiles: one
+// wave forms the weights and dV, its partner dP, dS and dK, with the weights handed over
+// through LDS).  Both sweeps use the forward's register layouts: the MFMA column is the row
+// that owns the accumulator (a query for dQ, a key for dK/dV), weights go from the score
+// registers to the B operand as bf16, and the transposed A operands (K^T for dQ; dO^T and
+// Q^T for dK/dV) come from row-major LDS tiles through ds_read_b64_tr_b16.  Masked pairs
+// get weight 0 by selection, so padding never enters a sum whatever it holds.
 //
 // Grouped K/V heads: dQ reads the shared K/V slice; one dK/dV workgroup sweeps the query
 // tiles of every query head of its group in turn, so the sum over the group stays in
@@ -253,7 +254,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 }
 
 // ------------------------------------------------------------------------ dK, dV
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+// Eight waves in four pairs; pair p owns the keys k0 + 32 p .. +31 of the workgroup's 128.
+// In each step (one 64-query tile) the V-wave of a pair (waves 0-3) forms S = Q K^T and the
+// weights P of its keys and hands P to its partner through LDS, while the K-wave (waves 4-7,
+// on the same SIMD) forms dP = dO V^T.  After a barrier the V-wave accumulates dV += dO^T P
+// and the K-wave dS = P (dP - D), dK += Q^T dS.  Each wave issues 32 MFMAs per step, and the
+// two waves of a SIMD cover each other's latencies.
+constexpr int kPairThreads = 512;
+__global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     const int32_t* __restrict__ lens, float* __restrict__ dK, float* __restrict__ dV, int B,
@@ -262,6 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 Gs[2][kTileElems];
   __shared__ __attribute__((aligned(16))) float Ls[2][kTile];  // log2-unit LSE; +inf on padding
   __shared__ __attribute__((aligned(16))) float Ds[2][kTile];
+  __shared__ __attribute__((aligned(16))) float Ps[4][2][16][64];  // [pair][block][register][lane]
   constexpr int kBK = 128;
 
   const int HB = Hkv * B;
@@ -272,11 +281,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int L = clamp_len(lens, b, n);
   const size_t kv_base = (size_t)bhk * n * kD;
   const int k0 = kt * kBK;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hl = lane >> 5, lq = lane & 31;
-  const int kj = k0 + 32 * w + lq;  // this lane's key
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, lq = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = w & 3;
+  const bool vwave = w < 4;
+  const int kj = k0 + 32 * pair + lq;  // this lane's key
 
   if (k0 >= L) {
-    for (int i = tid; i < kBK * kD / 4; i += kThreads) {
+    for (int i = tid; i < kBK * kD / 4; i += kPairThreads) {
       const int r = k0 + (i * 4) / kD;
       if (r < n) {
         *reinterpret_cast<floatx4*>(dK + kv_base + (size_t)r * kD + (i * 4) % kD) = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -287,17 +299,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
 
   const uint32_t valid_bytes = (uint32_t)L * kD * 2;
-  const rsrc_t rk = make_rsrc(K + kv_base, valid_bytes);
-  const rsrc_t rv = make_rsrc(V + kv_base, valid_bytes);
-
-  bf16x8 kop[8], vop[8];  // K^T and V^T operands of this lane's key
+  // the V-wave's operand is this lane's key row of K (for S), the K-wave's its row of V (dP)
+  const rsrc_t rop = make_rsrc((vwave ? K : V) + kv_base, valid_bytes);
+  bf16x8 op[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    kop[ks] = load_b128(rk, (kj * kD + 16 * ks + 8 * hl) * 2);
-    vop[ks] = load_b128(rv, (kj * kD + 16 * ks + 8 * hl) * 2);
-  }
+  for (int ks = 0; ks < 8; ++ks) op[ks] = load_b128(rop, (kj * kD + 16 * ks + 8 * hl) * 2);
   const bool key_ok = kj < L;
-  const int wave_k_first = k0 + 32 * w, wave_k_last = wave_k_first + 31;
+  const int wave_k_first = k0 + 32 * pair, wave_k_last = wave_k_first + 31;
 
   // query tiles [t0, t1) of each of the G query heads, swept head after head: step `it`
   // is tile t0 + it % nt of head it / nt
@@ -306,112 +314,166 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int t1 = (qend + kTile - 1) / kTile;
   const int nt = t1 - t0;
   const int steps = G * nt;
-  const TileFill fill(w, lane);
+  // tile fill by eight waves: wave w writes the 1 KiB slices 2w, 2w+1 of each tile
+  int src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (2 * w + i) + (lane >> 4);
+    const int pc = lane & 15;
+    const int c = pc ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    src[i] = (r * kD + 8 * c) * 2;
+  }
   auto issue = [&](int it, int buf) {
     const int bh = bh0 + it / nt, t = t0 + it % nt;
     const size_t base = (size_t)bh * n * kD;
-    fill.issue(make_rsrc(Q + base, valid_bytes), Qs[buf], t, w);
-    fill.issue(make_rsrc(dO + base, valid_bytes), Gs[buf], t, w);
+    const rsrc_t rq = make_rsrc(Q + base, valid_bytes);
+    const rsrc_t rg = make_rsrc(dO + base, valid_bytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      load_lds16(rq, (lds_void*)&Qs[buf][(2 * w + i) * 512], t * kTile * kD * 2 + src[i]);
+      load_lds16(rg, (lds_void*)&Gs[buf][(2 * w + i) * 512], t * kTile * kD * 2 + src[i]);
+    }
     if (tid < kTile) {
       const int q = t * kTile + tid;
       Ls[buf][tid] = q < L ? LSE[(size_t)bh * n + q] * ATTN_LOG2E : INFINITY;
       Ds[buf][tid] = q < L ? Dv[(size_t)bh * n + q] : 0.f;
     }
   };
+  auto skip = [&](int t, int qb) {
+    const int q0 = t * kTile + 32 * qb;
+    return (causal && q0 + 31 < wave_k_first) ||  // every query of the block precedes every key
+           (window && q0 - wave_k_last >= window);  // every query is past every key's window
+  };
+  auto masked = [&](int t, int qb) {
+    const int q0 = t * kTile + 32 * qb;
+    return !key_ok || (k0 + kBK > L) || (causal && q0 < wave_k_last) ||
+           (window && q0 + 31 - wave_k_first >= window);
+  };
 
-  floatx16 ak[4], av[4];  // dK^T, dV^T: lane holds d = 32 db + 8 (r/4) + 4 hl + r%4 of key kj
+  floatx16 acc[4];  // dV^T (V-wave) or dK^T (K-wave): lane holds d = 32 db + 8 (r/4) + 4 hl + r%4 of key kj
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ak[db][r] = 0.f;
-      av[db][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int it = 0; it < steps; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < steps) issue(it + 1, buf ^ 1);
-    const int t = t0 + it % nt;
-    const bf16* Qt = Qs[buf];
-    const bf16* Gt = Gs[buf];
+  if (vwave) {
+    for (int it = 0; it < steps; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < steps) issue(it + 1, buf ^ 1);
+      const int t = t0 + it % nt;
+      const bf16* Qt = Qs[buf];
+      const bf16* Gt = Gs[buf];
+      bf16x8 pop[2][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int q0 = t * kTile + 32 * qb;
-      if (causal && q0 + 31 < wave_k_first) continue;  // every query of the block precedes every key
-      if (window && q0 - wave_k_last >= window) continue;  // every query is past every key's window
-      floatx16 s, dp;  // S and dP: lane holds query q0 + 8 (r/4) + 4 hl + r%4 of key kj
+      for (int qb = 0; qb < 2; ++qb) {
+        if (skip(t, qb)) continue;
+        const int q0 = t * kTile + 32 * qb;
+        floatx16 s;  // S: lane holds query q0 + 8 (r/4) + 4 hl + r%4 of key kj
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qt[sw_slot(32 * qb + lq, 2 * ks + hl)]);
-        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gt[sw_slot(32 * qb + lq, 2 * ks + hl)]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[ks], dp, 0, 0, 0);
-      }
-      const bool need_mask = !key_ok || (k0 + kBK > L) || (causal && q0 < wave_k_last) ||
-                             (window && q0 + 31 - wave_k_first >= window);
-      bf16x8 pop[2], dsop[2];
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qt[sw_slot(32 * qb + lq, 2 * ks + hl)]);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, op[ks], s, 0, 0, 0);
+        }
+        const bool need_mask = masked(t, qb);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const floatx4 l4 = *reinterpret_cast<const floatx4*>(&Ls[buf][32 * qb + 8 * a + 4 * hl]);
-        const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds[buf][32 * qb + 8 * a + 4 * hl]);
-        floatx4 p4, ds4;
+        for (int a = 0; a < 4; ++a) {
+          const floatx4 l4 = *reinterpret_cast<const floatx4*>(&Ls[buf][32 * qb + 8 * a + 4 * hl]);
+          floatx4 p4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * a + c;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l4[c]));  // 0 on padding rows
-          if (need_mask) {
-            const int q = q0 + 8 * a + 4 * hl + c;
-            const bool ok = key_ok && (!causal || kj <= q) && (!window || kj > q - window);
-            p = ok ? p : 0.f;
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * a + c;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l4[c]));  // 0 on padding rows
+            if (need_mask) {
+              const int q = q0 + 8 * a + 4 * hl + c;
+              const bool ok = key_ok && (!causal || kj <= q) && (!window || kj > q - window);
+              p = ok ? p : 0.f;
+            }
+            p4[c] = p;
+            Ps[pair][qb][r][lane] = p;
           }
-          p4[c] = p;
-          ds4[c] = p * (dp[r] - d4[c]);
-        }
-        const bf16x4 pb = __builtin_convertvector(p4, bf16x4);
-        const bf16x4 db4 = __builtin_convertvector(ds4, bf16x4);
+          const bf16x4 pb = __builtin_convertvector(p4, bf16x4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {  // register 4a + c is element 4 (a%2) + c of group a/2
-          pop[a >> 1][4 * (a & 1) + c] = pb[c];
-          dsop[a >> 1][4 * (a & 1) + c] = db4[c];
+          for (int c = 0; c < 4; ++c) pop[qb][a >> 1][4 * (a & 1) + c] = pb[c];  // register 4a + c
         }
       }
-      // dV^T += dO^T P ; dK^T += Q^T dS
+      __syncthreads();  // the weights are in LDS for the K-waves
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int qb = 0; qb < 2; ++qb) {
+        if (skip(t, qb)) continue;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          av[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Gt, 2 * qb + g, db, lane), pop[g], av[db], 0, 0, 0);
-          ak[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Qt, 2 * qb + g, db, lane), dsop[g], ak[db], 0, 0, 0);
-        }
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int db = 0; db < 4; ++db)  // dV^T += dO^T P
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Gt, 2 * qb + g, db, lane), pop[qb][g], acc[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  } else {
+    for (int it = 0; it < steps; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < steps) issue(it + 1, buf ^ 1);
+      const int t = t0 + it % nt;
+      const bf16* Qt = Qs[buf];
+      const bf16* Gt = Gs[buf];
+      floatx16 dp[2];  // dP: lane holds query q0 + 8 (r/4) + 4 hl + r%4 of key kj
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (skip(t, qb)) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gt[sw_slot(32 * qb + lq, 2 * ks + hl)]);
+          dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, op[ks], dp[qb], 0, 0, 0);
+        }
+      }
+      __syncthreads();  // the V-waves' weights are in LDS
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (skip(t, qb)) continue;
+        bf16x8 dsop[2];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds[buf][32 * qb + 8 * a + 4 * hl]);
+          floatx4 ds4;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * a + c;
+            ds4[c] = Ps[pair][qb][r][lane] * (dp[qb][r] - d4[c]);
+          }
+          const bf16x4 db4 = __builtin_convertvector(ds4, bf16x4);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) dsop[a >> 1][4 * (a & 1) + c] = db4[c];  // register 4a + c
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int db = 0; db < 4; ++db)  // dK^T += Q^T dS
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Qt, 2 * qb + g, db, lane), dsop[g], acc[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   if (kj < n) {
-    float* krow = dK + kv_base + (size_t)kj * kD;
-    float* vrow = dV + kv_base + (size_t)kj * kD;
+    float* row = (vwave ? dV : dK) + kv_base + (size_t)kj * kD;
+    const float f = vwave ? 1.f : scale;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        floatx4 xk, xv;
+        floatx4 x;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          xk[c] = key_ok ? ak[db][4 * a + c] * scale : 0.f;
-          xv[c] = key_ok ? av[db][4 * a + c] : 0.f;
-        }
-        *reinterpret_cast<floatx4*>(krow + 32 * db + 8 * a + 4 * hl) = xk;
-        *reinterpret_cast<floatx4*>(vrow + 32 * db + 8 * a + 4 * hl) = xv;
+        for (int c = 0; c < 4; ++c) x[c] = key_ok ? acc[db][4 * a + c] * f : 0.f;
+        *reinterpret_cast<floatx4*>(row + 32 * db + 8 * a + 4 * hl) = x;
       }
   }
 }
@@ -442,7 +504,7 @@ hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_ktiles = (n + 127) / 128;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)n_ktiles * batch * kv_heads), dim3(kThreads),
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)n_ktiles * batch * kv_heads), dim3(kPairThreads),
                      0, stream, q, k, v, dout, lse, Dv, seq_lens, dk, dv, batch, heads, kv_heads,
                      n, causal, window, c_log2, scale);
   return hipGetLastError();
