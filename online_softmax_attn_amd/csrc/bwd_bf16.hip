@@ -270,7 +270,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 Gs[2][kTileElems];
   __shared__ __attribute__((aligned(16))) float Ls[2][kTile];  // log2-unit LSE; +inf on padding
   __shared__ __attribute__((aligned(16))) float Ds[2][kTile];
-  __shared__ __attribute__((aligned(16))) float Ps[4][2][16][64];  // [pair][block][register][lane]
+  // weights handed from V-wave to K-wave: [pair][block][register group][lane], four fp32 each
+  __shared__ __attribute__((aligned(16))) floatx4 Ps[4][2][4][64];
   constexpr int kBK = 128;
 
   const int HB = Hkv * B;
@@ -395,8 +396,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
               p = ok ? p : 0.f;
             }
             p4[c] = p;
-            Ps[pair][qb][r][lane] = p;
           }
+          Ps[pair][qb][a][lane] = p4;
           const bf16x4 pb = __builtin_convertvector(p4, bf16x4);
 #pragma unroll
           for (int c = 0; c < 4; ++c) pop[qb][a >> 1][4 * (a & 1) + c] = pb[c];  // register 4a + c
@@ -442,12 +443,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds[buf][32 * qb + 8 * a + 4 * hl]);
+          const floatx4 p4 = Ps[pair][qb][a][lane];
           floatx4 ds4;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int r = 4 * a + c;
-            ds4[c] = Ps[pair][qb][r][lane] * (dp[qb][r] - d4[c]);
-          }
+          for (int c = 0; c < 4; ++c) ds4[c] = p4[c] * (dp[qb][4 * a + c] - d4[c]);
           const bf16x4 db4 = __builtin_convertvector(ds4, bf16x4);
 #pragma unroll
           for (int c = 0; c < 4; ++c) dsop[a >> 1][4 * (a & 1) + c] = db4[c];  // register 4a + c
