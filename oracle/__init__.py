@@ -25,6 +25,11 @@ Functions and their pins (tests/test_oracle.py):
   online_softmax_scalar / merge / summarize / blocked_softmax
       pinned by the worked example's step table (and its wrong variant), the block-merge
       experiment design of el-ai.com section 4, and merge associativity/commutativity.
+  merge_outputs
+      pinned by attention over the union of disjoint key sets (plain and causal, key sets
+      of uneven size and scores up to ~+-1000), the causal decomposition of a sequence into
+      query/key chunks, part-order invariance, empty parts, and the closed form for two
+      parts of equal LSE (mean of the outputs, LSE + ln 2).
   attention_grad (backward.py)
       pinned by 50-digit central differences of the forward definition (masks, padding)
       (also two query heads sharing one K/V head under a causal window) and by closed forms
@@ -42,7 +47,7 @@ No function here is "parity unpinned".
 from . import fp8
 from .attention import attend, attention, attention_rows, decode, to_f64
 from .backward import attention_grad
-from .online import blocked_softmax, merge, online_softmax_scalar, summarize
+from .online import blocked_softmax, merge, merge_outputs, online_softmax_scalar, summarize
 
 __all__ = [
     "fp8",
@@ -54,6 +59,7 @@ __all__ = [
     "attention_grad",
     "online_softmax_scalar",
     "merge",
+    "merge_outputs",
     "summarize",
     "blocked_softmax",
 ]

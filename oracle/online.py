@@ -75,3 +75,31 @@ def blocked_softmax(scores, values, block: int):
         state = part if state is None else merge(state, part)
     m, l, u = state
     return u / l
+
+
+def merge_outputs(outs, lses):
+    """Attention over the union of disjoint key sets from each set's output and LSE.
+
+    outs: [S, rows, d] outputs, each normalised over its own keys; lses: [S, rows] natural
+    log-sum-exp of each set's scaled scores (-inf where a set admits no key of the row).
+    A part (o_s, L_s) is the summary (m, l, u) = (L_s, 1, o_s) of el-ai.com section 2 (the
+    reference may be any constant), and the parts fold with the section-4 merge above.
+    Returns (o [rows, d], lse [rows]); rows no part admits give o = 0, lse = -inf.
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    S, rows, d = outs.shape
+    o = np.zeros((rows, d))
+    lse = np.full(rows, -np.inf)
+    for r in range(rows):
+        state = None
+        for s in range(S):
+            if not np.isfinite(lses[s, r]):
+                continue  # a set with no admitted key contributes nothing
+            part = (float(lses[s, r]), 1.0, outs[s, r])
+            state = part if state is None else merge(state, part)
+        if state is not None:
+            m, l, u = state
+            o[r] = u / l
+            lse[r] = m + math.log(l)
+    return o, lse
