@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -208,6 +208,29 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const 
                          const float* k_scale, const float* v_scale, void* o, float* lse,
                          const int32_t* seq_lens, int batch, int heads, int kv_heads,
                          int seq_len, int head_dim, int causal, float scale, void* stream);
+
+/*
+ * attn_merge — attention over the union of disjoint key sets from each set's own result
+ * (el-ai.com "Attenzione: softmax online, riscalamento e memoria", section 4: summaries of
+ * disjoint blocks of keys combine by bringing them to the larger maximum and adding).  A
+ * part is an output o_s normalised over its own keys and that set's log-sum-exp lse_s, as
+ * attn_fwd writes them; the merged row is
+ *     lse = ln sum_s exp(lse_s),     o = sum_s exp(lse_s - lse) o_s.
+ * It joins the pieces of one query block computed against different key ranges — the
+ * per-device step of attention over a sequence whose keys are spread over devices.
+ *
+ * o_parts   : [parts, rows, head_dim] (dtype), the parts stacked; rows is any row count
+ *             (for example batch * heads * seq_len).
+ * lse_parts : fp32 [parts, rows], natural log; -inf where a part admits no key of the row
+ *             (its output values are then never used: they may hold anything).
+ * o         : [rows, head_dim] (dtype), written in full; must not overlap o_parts.  Rows no
+ *             part admits get 0.
+ * lse       : optional fp32 [rows]; -inf where no part admits the row.
+ * Supported : dtype bf16 or f32 (merged in fp32, o rounded to nearest even for bf16),
+ *             head_dim 64 or 128, 1 <= parts <= 1024.
+ */
+attn_status attn_merge(attn_dtype dtype, const void* o_parts, const float* lse_parts, void* o,
+                       float* lse, int parts, int64_t rows, int head_dim, void* stream);
 
 /* attn_status_str — static, NUL-terminated name of a status code (never NULL). */
 const char* attn_status_str(attn_status status);

@@ -8,6 +8,7 @@ Entry points mirror the C ABI in include/attn.h:
     attn_decode_workspace_bytes   workspace size the decode needs
     attn_quantize_fp8             bf16 -> FP8 E4M3 codes with one scale per 64-row block
     attn_fwd_fp8                  prefill on E4M3 operands (bf16 output)
+    attn_merge                    join results over disjoint key sets by their lse
     attn_status_str, attn_abi_version
 """
 
@@ -23,6 +24,7 @@ from .binding import (
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_fwd_fp8,
+    attn_merge,
     attn_quantize_fp8,
     attn_status_str,
     lib,
@@ -40,6 +42,7 @@ __all__ = [
     "attn_decode_workspace_bytes",
     "attn_fwd",
     "attn_fwd_fp8",
+    "attn_merge",
     "attn_quantize_fp8",
     "attn_status_str",
     "lib",

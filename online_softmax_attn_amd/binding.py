@@ -42,6 +42,7 @@ SIGNATURES = {
     "attn_quantize_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                           ctypes.c_float, _P]),
+    "attn_merge": (_I, [_I, _P, _P, _P, _P, _I, ctypes.c_int64, _I, _P]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
 }
@@ -170,6 +171,40 @@ def attn_fwd(q, k, v, *, causal=False, window=0, scale=None, seq_lens=None, out=
                         _stream(stream))
     if st != ATTN_OK:
         raise AttnError("attn_fwd", st)
+    return (out, lse) if return_lse else out
+
+
+def attn_merge(o_parts, lse_parts, *, out=None, lse=None, return_lse=False, stream=None):
+    """Attention over the union of disjoint key sets from each set's (o, lse).
+
+    o_parts: [S, ..., d] (bf16 or fp32, d in {64, 128}), the S parts stacked on the first
+    dimension; lse_parts: fp32 [S, ...] with the same leading shape (-inf where a part admits
+    no key of the row).  Returns o [..., d], or (o, lse) with return_lse.
+    """
+    _check_dev("o_parts", o_parts)
+    _check_dev("lse_parts", lse_parts, torch.float32)
+    if o_parts.dtype not in _DT:
+        raise ValueError("o_parts must be float32 or bfloat16")
+    if o_parts.dim() < 2 or tuple(lse_parts.shape) != tuple(o_parts.shape[:-1]):
+        raise ValueError("o_parts must be [S, ..., d] and lse_parts [S, ...]")
+    S, d = int(o_parts.shape[0]), int(o_parts.shape[-1])
+    rows = o_parts.numel() // (S * d) if S * d else 0
+    if out is None:
+        out = torch.empty(o_parts.shape[1:], dtype=o_parts.dtype, device=o_parts.device)
+    _check_dev("out", out, o_parts.dtype)
+    if tuple(out.shape) != tuple(o_parts.shape[1:]):
+        raise ValueError("out must be o_parts.shape[1:]")
+    if lse is None and return_lse:
+        lse = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=o_parts.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if tuple(lse.shape) != tuple(lse_parts.shape[1:]):
+            raise ValueError("lse must be lse_parts.shape[1:]")
+    st = lib().attn_merge(_DT[o_parts.dtype], o_parts.data_ptr(), lse_parts.data_ptr(),
+                          out.data_ptr(), lse.data_ptr() if lse is not None else None, S, rows,
+                          d, _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError("attn_merge", st)
     return (out, lse) if return_lse else out
 
 

@@ -135,6 +135,19 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const 
       reinterpret_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_merge(attn_dtype dtype, const void* o_parts, const float* lse_parts, void* o,
+                       float* lse, int parts, int64_t rows, int head_dim, void* stream) {
+  if (!o_parts || !lse_parts || !o) return ATTN_ERR_INVALID;
+  if (parts <= 0 || rows <= 0 || head_dim <= 0) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (parts > 1024) return ATTN_ERR_UNSUPPORTED;
+  if ((rows + 15) / 16 >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;  // grid: >= 16 rows per workgroup
+  return launch_status(launch_merge(dtype == ATTN_BF16, o_parts, lse_parts, o, lse, parts,
+                                    (long long)rows, head_dim,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t attn_decode_workspace_bytes(int batch, int heads, int kv_heads, int head_dim,
                                    int max_seq_len, int window, int kv_split) {
   if (batch <= 0 || heads <= 0 || head_dim != 128 || max_seq_len <= 0) return 0;

@@ -62,6 +62,12 @@ hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v
                           bf16* o, float* lse, const int32_t* seq_lens, int batch, int heads,
                           int kv_heads, int n, int causal, float scale, hipStream_t stream);
 
+// Merge of results over disjoint key sets: parts [n_parts, rows, head_dim] (bf16 or fp32)
+// with their fp32 lse [n_parts, rows] into out [rows, head_dim] and lse_out [rows].
+hipError_t launch_merge(bool bf16_data, const void* parts, const float* lse_parts, void* out,
+                        float* lse_out, int n_parts, long long rows, int head_dim,
+                        hipStream_t stream);
+
 // ---------------------------------------------------------------------------------------
 // Buffer resources: loads through a buffer descriptor return 0 for any byte offset at or
 // past `bytes`, which is how out-of-range rows (ragged tails, padding) are zero-filled

@@ -174,3 +174,20 @@ def f8(**kw):
 ])
 def test_fwd_fp8_validation(kw, status):
     assert f8(**kw) == status
+
+
+def mg(**kw):
+    a = dict(dt=attn.ATTN_BF16, parts=FAKE, lses=FAKE, o=FAKE, lse=None, S=4, rows=1000, d=128)
+    a.update(kw)
+    return attn.lib().attn_merge(a["dt"], a["parts"], a["lses"], a["o"], a["lse"], a["S"], a["rows"],
+                                 a["d"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(parts=None), INVALID), (dict(lses=None), INVALID), (dict(o=None), INVALID),
+    (dict(S=0), INVALID), (dict(rows=0), INVALID), (dict(rows=-5), INVALID), (dict(d=0), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(dt=7), UNSUPPORTED), (dict(S=1025), UNSUPPORTED),
+    (dict(rows=1 << 36), UNSUPPORTED),
+])
+def test_merge_validation(kw, status):
+    assert mg(**kw) == status
