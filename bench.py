@@ -33,6 +33,10 @@ oracle timed on this host over a bounded sample of the prefill workload.
                   block quantisation of Q, K, V (attn_quantize_fp8) timed apart; timed and
                   reported like the bf16 prefill (warm, plus a cold reference); the
                   roofline is the dense fp8 MFMA peak.
+--workload cp     one device's share of sequence-parallel causal attention over the
+                  [1, 32, 32768, 128] workload: 16 chunks for 8 devices (zig-zag), device 0's
+                  17 chunk pairs through attn_fwd and their two attn_merge calls (the K/V
+                  exchange between devices is not part of it).
 --profile-pass    runs one 1 GiB device copy, one prefill and one decode and exits (the
                   command the rocprofv3 counter and trace runs wrap).
 --record-traffic FETCH_CSV WRITE_CSV
@@ -289,6 +293,77 @@ def bench_fp8(args):
         "quantize_ms_avg": round(q_ms, 5)}))
 
 
+def bench_cp(args):
+    """One device's share of sequence-parallel causal attention over the long-context workload.
+
+    [1, 32, 32768, 128] cut into 2G = 16 chunks of 2048 tokens for G = 8 devices, device g
+    owning query chunks g and 2G-1-g (zig-zag: every device gets 17 chunk pairs).  For an
+    owned chunk c the share is attn_fwd of Q_c against K/V chunks 0..c (no mask off the
+    diagonal, causal on it) and one attn_merge of those c+1 results.  All chunks are
+    resident on this one GPU: the exchange of K/V chunks between devices is not part of it.
+    """
+    import torch
+
+    import online_softmax_attn_amd as attn
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.long_prefill()
+    q, k, v = w["q"].to(dev), w["k"].to(dev), w["v"].to(dev)
+    B, H, n, d = q.shape
+    G, g_dev = 8, 0
+    C = 2 * G
+    c = n // C
+    chunk = lambda t, j: t[:, :, j * c:(j + 1) * c].contiguous()
+    owned = [g_dev, C - 1 - g_dev]
+    Qc = {i: chunk(q, i) for i in owned}
+    Kc = [chunk(k, j) for j in range(max(owned) + 1)]
+    Vc = [chunk(v, j) for j in range(max(owned) + 1)]
+    del q, k, v
+    parts = {i: torch.empty(i + 1, B, H, c, d, dtype=torch.bfloat16, device=dev) for i in owned}
+    lses = {i: torch.empty(i + 1, B, H, c, dtype=torch.float32, device=dev) for i in owned}
+    outs = {i: torch.empty(B, H, c, d, dtype=torch.bfloat16, device=dev) for i in owned}
+    out_lse = {i: torch.empty(B, H, c, dtype=torch.float32, device=dev) for i in owned}
+
+    def step():
+        for i in owned:
+            for j in range(i + 1):
+                attn.attn_fwd(Qc[i], Kc[j], Vc[j], causal=(j == i), out=parts[i][j], lse=lses[i][j])
+            attn.attn_merge(parts[i], lses[i], out=outs[i], lse=out_lse[i])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    step()  # untimed: keeps the GPU busy while the event and the burst are enqueued
+    ev[0].record()
+    for _ in range(args.steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    full = 4.0 * d * B * H * c * c                  # an unmasked chunk pair
+    diag = 4.0 * d * B * H * c * (c + 1) / 2        # a causal diagonal chunk
+    n_full = sum(owned)
+    flops = n_full * full + len(owned) * diag
+    tf = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "sequence-parallel causal attention: one device's share, TFLOPS",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V of the long-context workload)",
+        "config": {"workload": f"causal prefill B=1 H=32 n=32768 d=128 in {C} chunks of {c} for "
+                               f"{G} devices (zig-zag); device {g_dev}: query chunks {owned}, "
+                               f"{n_full} unmasked + {len(owned)} causal chunk pairs + "
+                               f"{len(owned)} merges; K/V exchange not included"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "ms_avg": round(ms, 5)}))
+
+
 def main():
     if len(sys.argv) == 4 and sys.argv[1] == "--record-traffic":
         record_traffic(sys.argv[2], sys.argv[3])
@@ -300,7 +375,7 @@ def main():
     # right after 5 warm-up steps runs ~15% slower than the same burst 30 ms later), so the
     # default warm-up keeps the GPU busy for ~60 ms before anything is timed.
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", choices=["prefill", "long", "backward", "grouped", "window", "fp8"],
+    ap.add_argument("--workload", choices=["prefill", "long", "backward", "grouped", "window", "fp8", "cp"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -325,6 +400,8 @@ def main():
         return bench_backward(args)
     if args.workload == "fp8":
         return bench_fp8(args)
+    if args.workload == "cp":
+        return bench_cp(args)
     window, kv_heads = 0, 32
     dec_cfg = " + paged decode B=32 H=32 d=128 lens U[1024,8192] block 16"
     if args.workload == "long":

@@ -6,9 +6,11 @@
 // log-sum-exp lse_s, i.e. the summary (lse_s, 1, o_s); folding all parts against
 // m* = max_s lse_s gives
 //     l = sum_s exp(lse_s - m*),   o = sum_s exp(lse_s - m*) o_s / l,   lse = m* + ln l.
-// Parts with lse_s = -inf admit no key of the row and are skipped by selection, so whatever
-// their output holds never enters the sum.
+// Parts with lse_s = -inf admit no key of the row and are skipped, so whatever their output
+// holds never enters the sum.
 //
+// The parts are folded in one pass with a running maximum (section 2's recurrence applied to
+// whole parts): a part above the maximum raises it and rescales what is already summed.
 // Layout: 8 consecutive elements of a row per lane (16 bytes of bf16, 32 of fp32), d / 8
 // lanes per row; each lane walks the parts with four loads in flight.  The kernel streams
 // parts x rows x d elements once and is bound by HBM.
@@ -56,32 +58,31 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const T* __restrict__ p
   const int col = 8 * (threadIdx.x % kLanes);
   if (row >= rows) return;  // no barriers below
 
-  float m = -INFINITY;
-  for (int s = 0; s < n_parts; ++s) m = __builtin_fmaxf(m, lse_parts[(long long)s * rows + row]);
-
+  // one pass over the parts with the running maximum of section 2: a part above it raises
+  // it and rescales what is already summed; four parts' loads are in flight together
+  float m = -INFINITY, l = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-  if (m > -INFINITY) {  // some part admits a key of this row
-    for (int s0 = 0; s0 < n_parts; s0 += kUnroll) {
-      float x[kUnroll][8], w[kUnroll];
-      bool live[kUnroll];
+  for (int s0 = 0; s0 < n_parts; s0 += kUnroll) {
+    float x[kUnroll][8], ls[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int s = s0 + u;
-        live[u] = s < n_parts;
-        const float ls = live[u] ? lse_parts[(long long)s * rows + row] : -INFINITY;
-        live[u] = ls > -INFINITY;
-        w[u] = live[u] ? __builtin_amdgcn_exp2f((ls - m) * ATTN_LOG2E) : 0.f;
-        if (s < n_parts) load8(parts + ((long long)s * rows + row) * D + col, x[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (s0 + u >= n_parts) break;
-        l += w[u];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = live[u] ? fmaf(w[u], x[u][e], acc[e]) : acc[e];
-      }
+    for (int u = 0; u < kUnroll; ++u) {
+      const int s = s0 + u;
+      ls[u] = s < n_parts ? lse_parts[(long long)s * rows + row] : -INFINITY;
+      if (s < n_parts) load8(parts + ((long long)s * rows + row) * D + col, x[u]);
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (!(ls[u] > -INFINITY)) continue;  // the part admits no key of this row
+      const float m_new = __builtin_fmaxf(m, ls[u]);
+      const float f = __builtin_amdgcn_exp2f((m - m_new) * ATTN_LOG2E);  // 0 from the empty state
+      const float w = __builtin_amdgcn_exp2f((ls[u] - m_new) * ATTN_LOG2E);
+      l = fmaf(l, f, w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[u][e], acc[e] * f);
+      m = m_new;
+    }
+  }
+  if (m > -INFINITY) {
     const float inv = 1.0f / l;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= inv;
