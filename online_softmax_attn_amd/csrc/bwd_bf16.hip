@@ -125,8 +125,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   constexpr int kBM = 128;
 
   const int HB = H * B;
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / HB);  // heaviest causal tiles first
-  const int bh = blockIdx.x % HB;
+  const GridSlot slot = causal_grid_slot((int)blockIdx.x, HB, n_qtiles);  // heaviest first
+  const int qt = n_qtiles - 1 - slot.rank;
+  const int bh = slot.bh;
   const int L = clamp_len(lens, bh / H, n);
   const size_t base = (size_t)bh * n * kD;
   const size_t kv_base = ((size_t)(bh / H) * Hkv + (bh % H) / (H / Hkv)) * n * kD;
@@ -275,8 +276,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
   constexpr int kBK = 128;
 
   const int HB = Hkv * B;
-  const int kt = (int)(blockIdx.x / HB);  // key block 0 has the most causal work: first
-  const int bhk = blockIdx.x % HB;        // b * Hkv + K/V head
+  const GridSlot slot = causal_grid_slot((int)blockIdx.x, HB, (n + kBK - 1) / kBK);
+  const int kt = slot.rank;  // key block 0 has the most causal work: first
+  const int bhk = slot.bh;   // b * Hkv + K/V head
   const int b = bhk / Hkv, G = H / Hkv;
   const int bh0 = b * H + (bhk % Hkv) * G;  // first query head of the group
   const int L = clamp_len(lens, b, n);

@@ -69,6 +69,32 @@ hipError_t launch_merge(bool bf16_data, const void* parts, const float* lse_part
                         hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------
+// Launch order of a causal grid: `n_tiles` work tiles per (batch, head), `HB` (batch, head)s,
+// one workgroup each.  Workgroups are dealt round-robin to the 8 XCDs (block % 8), so XCD x
+// receives blocks x, x+8, ...  Each XCD gets a contiguous range of HB/8 (batch, head)s, taken
+// eight at a time: all tiles of eight heads, heaviest first, before the next eight.  About 64
+// workgroups are resident per XCD (32 CUs, two each), so few heads are in flight on one XCD
+// and their K/V are mostly re-read from its 4 MiB L2, while the heavy tiles of a group still
+// start early enough to keep the tail short.  Measured on the causal prefill [4,32,2048,128]
+// (16 heads per XCD): reads from MALL/HBM of 353 MB per launch against 599 MB when all 16
+// heads of an XCD run at once, 1-3% faster; groups of four read only the compulsory 202 MB
+// but run 1-5% slower (their last group's heavy tiles lengthen the tail).  `rank` is the
+// tile's place in heaviness order (0 = most work).
+struct GridSlot {
+  int rank;
+  int bh;
+};
+__device__ __forceinline__ GridSlot causal_grid_slot(int block, int HB, int n_tiles) {
+  constexpr int kGroup = 8;
+  if (HB % (8 * kGroup) == 0) {
+    const int x = block % 8, i = block / 8, span = kGroup * n_tiles;
+    return {(i % span) / kGroup, x * (HB / 8) + (i / span) * kGroup + i % kGroup};
+  }
+  const int j = block % HB;  // all tiles of one rank, then the next
+  return {block / HB, (HB % 8 == 0) ? (j % 8) * (HB / 8) + j / 8 : j};
+}
+
+// ---------------------------------------------------------------------------------------
 // Buffer resources: loads through a buffer descriptor return 0 for any byte offset at or
 // past `bytes`, which is how out-of-range rows (ragged tails, padding) are zero-filled
 // without branches.  The fourth descriptor word is the gfx9-family default format.

@@ -28,11 +28,11 @@
 //   * exp is v_exp_f32 (2^x): scores are scaled by scale*log2(e) inside one FMA.
 //   * the normaliser sums the bf16-ROUNDED weights that enter the P.V product (dot2 with
 //     ones), so rounding of P cancels in u/l to first order.
-//   * causal: tiles strictly above a wave's diagonal are skipped, the grid is issued
-//     heaviest-first, and every query tile of one (batch, head) lands on the same XCD
-//     (workgroups are dealt round-robin to the 8 XCDs) so K/V are re-read from one L2.
-//     Consecutive heads share an XCD too, so the query heads of one K/V group (grouped
-//     heads) read their shared K/V from one L2 as well.
+//   * causal: tiles strictly above a wave's diagonal are skipped; every query tile of one
+//     (batch, head) lands on the same XCD, eight heads at a time, heaviest tiles first
+//     (causal_grid_slot), so K/V are re-read from that XCD's L2.  Consecutive heads share an
+//     XCD, so the query heads of one K/V group (grouped heads) read their shared K/V from
+//     one L2 as well.
 //   * causal window w: the key loop starts at the first tile any query of the workgroup
 //     admits (query i admits keys i - w < j <= i); tiles that cross a window edge are
 //     masked like the diagonal ones.
@@ -93,10 +93,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 Vs[2][kTileElems];
 
   const int HB = H * B;
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / HB);  // heaviest causal tiles first
-  // slot j runs on XCD j % 8; give each XCD a contiguous range of (batch, head)s
-  const int j = blockIdx.x % HB;
-  const int bh = (HB % 8 == 0) ? (j % 8) * (HB / 8) + j / 8 : j;
+  const GridSlot slot = causal_grid_slot((int)blockIdx.x, HB, n_qtiles);
+  const int qt = n_qtiles - 1 - slot.rank;  // the last query tile has the most causal work
+  const int bh = slot.bh;
   const int b = bh / H;
   int L = lens ? lens[b] : n;
   L = L < 0 ? 0 : (L > n ? n : L);

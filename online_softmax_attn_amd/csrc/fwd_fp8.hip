@@ -71,9 +71,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t Vs[2][kTileBytes];
 
   const int HB = H * B;
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / HB);  // heaviest causal tiles first
-  const int j = blockIdx.x % HB;
-  const int bh = (HB % 8 == 0) ? (j % 8) * (HB / 8) + j / 8 : j;  // one XCD per (b, h) range
+  const GridSlot slot = causal_grid_slot((int)blockIdx.x, HB, n_qtiles);  // heaviest first
+  const int qt = n_qtiles - 1 - slot.rank;
+  const int bh = slot.bh;
   const int b = bh / H;
   const int bhk = b * Hkv + (bh % H) / (H / Hkv);
   int L = lens ? lens[b] : n;
