@@ -45,7 +45,8 @@ def check(got, ref, name):
 
 CASES = [(1, 1, 1, False, None), (1, 1, 64, False, None), (1, 2, 64, True, None),
          (2, 2, 130, True, None), (2, 2, 200, False, [77, 200]), (3, 2, 257, True, [1, 100, 257]),
-         (1, 4, 1000, True, None)]
+         (1, 4, 1000, True, None),
+         (2, 32, 200, True, [200, 77])]  # B*H a multiple of 64: eight heads per XCD at a time
 
 
 @pytest.mark.parametrize("B,H,n,causal,lens", CASES)

@@ -123,6 +123,7 @@ FP8_CASES = [
     (1, 1, 1, 1, False, None), (1, 2, 2, 64, True, None), (2, 2, 2, 130, True, None),
     (1, 3, 3, 127, False, None), (2, 4, 2, 300, True, [300, 129]), (3, 2, 1, 200, False, [1, 64, 200]),
     (1, 4, 4, 1000, True, None), (2, 8, 2, 257, True, None),
+    (2, 32, 8, 200, True, [200, 77]),  # B*H a multiple of 64: eight heads per XCD at a time
 ]
 
 

@@ -59,6 +59,7 @@ BF16_CASES = [
     (1, 4, 4, 1000, True, 1, None),           # window of one: every row returns its own value
     (1, 8, 1, 333, True, 1000, None),         # window longer than the sequence: plain causal
     (3, 4, 1, 200, True, 37, [1, 150, 200]),
+    (2, 32, 8, 300, True, 100, [300, 150]),  # B*H a multiple of 64: eight heads per XCD at a time
 ]
 
 

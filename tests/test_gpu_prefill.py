@@ -97,6 +97,8 @@ BF16_CASES = [
     (1, 1, 1, False, None), (1, 2, 17, True, None), (2, 2, 64, True, None), (1, 3, 127, False, None),
     (2, 1, 128, True, None), (1, 2, 129, True, None), (2, 2, 300, False, None), (1, 2, 300, True, None),
     (3, 2, 200, True, [1, 150, 200]), (2, 2, 257, False, [64, 129]), (1, 1, 1000, True, None),
+    # B*H a multiple of 64: the grid runs eight heads per XCD at a time
+    (2, 32, 300, True, [300, 77]), (1, 64, 130, False, None),
 ]
 
 
