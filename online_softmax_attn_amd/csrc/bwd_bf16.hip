@@ -157,6 +157,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   }
   const bool row_ok = qi < L;
   const float lse2 = row_ok ? LSE[(size_t)bh * n + qi] * ATTN_LOG2E : 0.f;
+  // admitted (this lane's query, key) pairs: lo <= qi - key < hi with lo = 0 when causal
+  // (else -n) and hi = window when one is set (else n); a padding query admits none
+  const int mask_lo = causal ? 0 : -n;
+  const int mask_hi = window ? window : n;
   const float Di = row_ok ? Dv[(size_t)bh * n + qi] : 0.f;
 
   const int kend = causal ? min(L, m0 + kBM) : L;
@@ -206,6 +210,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         }
       const bool need_mask = !row_ok || (k0 + kTile > L) || (causal && k0 + kTile - 1 > wave_q_first) ||
                              (window && k0 <= wave_q_last - window);
+      if (need_mask) {  // scores outside the mask become -inf, their weights 0
+        // element (kb, r) is key k0 + 4 hl + o with o = 32 kb + 8 (r/4) + r%4; admitted iff
+        // lo <= qi - key < hi (one unsigned compare) and key < L
+        const unsigned base = (unsigned)(qi - k0 - 4 * hl - mask_lo);
+        const unsigned mask_span = row_ok ? (unsigned)(mask_hi - mask_lo) : 0u;
+        const int o_lim = L - k0 - 4 * hl;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
+            const bool ok = base - (unsigned)o < mask_span && o < o_lim;
+            s[kb][r] = ok ? s[kb][r] : -INFINITY;
+          }
+      }
       bf16x8 dsop[4];
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
@@ -216,12 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int r = r0 + e + u;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -lse2));
-            if (need_mask) {
-              const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-              const bool ok = row_ok && key < L && (!causal || key <= qi) && (!window || key > qi - window);
-              p = ok ? p : 0.f;
-            }
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -lse2));  // 0 if masked
             d2[u] = p * (dp[kb][r] - Di);
           }
           const bf16x2 db2 = __builtin_convertvector(d2, bf16x2);
@@ -308,6 +322,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) op[ks] = load_b128(rop, (kj * kD + 16 * ks + 8 * hl) * 2);
   const bool key_ok = kj < L;
+  // admitted (query q, this lane's key) pairs: lo <= q - kj < hi with lo = 0 when causal
+  // (else -n) and hi = window when one is set (else n); a padding key admits none
+  const int mask_lo = causal ? 0 : -n;
+  const unsigned mask_span = key_ok ? (unsigned)((window ? window : n) - mask_lo) : 0u;
   const int wave_k_first = k0 + 32 * pair, wave_k_last = wave_k_first + 31;
 
   // query tiles [t0, t1) of each of the G query heads, swept head after head: step `it`
@@ -336,11 +354,14 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
       load_lds16(rq, (lds_void*)&Qs[buf][(2 * w + i) * 512], t * kTile * kD * 2 + src[i]);
       load_lds16(rg, (lds_void*)&Gs[buf][(2 * w + i) * 512], t * kTile * kD * 2 + src[i]);
     }
-    if (tid < kTile) {
-      const int q = t * kTile + tid;
-      Ls[buf][tid] = q < L ? LSE[(size_t)bh * n + q] * ATTN_LOG2E : INFINITY;
-      Ds[buf][tid] = q < L ? Dv[(size_t)bh * n + q] : 0.f;
-    }
+  };
+  // the tile's LSE (log2 units, +inf on padding) and D, one query per lane of wave 0: loaded
+  // into registers when the tile's loads are issued and written to LDS at the end of the
+  // step, so the wave never waits on them mid-step
+  auto load_ld = [&](int it, float& l, float& d) {
+    const int bh = bh0 + it / nt, q = (t0 + it % nt) * kTile + tid;
+    l = q < L ? LSE[(size_t)bh * n + q] * ATTN_LOG2E : INFINITY;
+    d = q < L ? Dv[(size_t)bh * n + q] : 0.f;
   };
   auto skip = [&](int t, int qb) {
     const int q0 = t * kTile + 32 * qb;
@@ -360,51 +381,67 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
   issue(0, 0);
+  if (tid < kTile) {
+    float l, d;
+    load_ld(0, l, d);
+    Ls[0][tid] = l;
+    Ds[0][tid] = d;
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   if (vwave) {
     for (int it = 0; it < steps; ++it) {
       const int buf = it & 1;
-      if (it + 1 < steps) issue(it + 1, buf ^ 1);
+      float l_next = 0.f, d_next = 0.f;
+      if (it + 1 < steps) {
+        issue(it + 1, buf ^ 1);
+        if (tid < kTile) load_ld(it + 1, l_next, d_next);
+      }
       const int t = t0 + it % nt;
       const bf16* Qt = Qs[buf];
       const bf16* Gt = Gs[buf];
-      bf16x8 pop[2][2];
+      // S of both 32-query blocks as two interleaved product chains (a block wholly outside
+      // the mask is computed too and masked to zero weights: no branch between the chains
+      // and the exps)
+      floatx16 s[2];  // S: lane holds query q0 + 8 (r/4) + 4 hl + r%4 of key kj
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qt[sw_slot(32 * qb + lq, 2 * ks + hl)]);
+          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, op[ks], s[qb], 0, 0, 0);
+        }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        if (skip(t, qb)) continue;
-        const int q0 = t * kTile + 32 * qb;
-        floatx16 s;  // S: lane holds query q0 + 8 (r/4) + 4 hl + r%4 of key kj
+        if (masked(t, qb)) {  // scores outside the mask become -inf, their weights 0
+          // element r is query q = q0 + 4 hl + 8 (r/4) + r%4, admitted iff lo <= q - kj < hi:
+          // one unsigned compare of (q - kj - lo) against the span per element
+          const unsigned base = (unsigned)(t * kTile + 32 * qb + 4 * hl - kj - mask_lo);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qt[sw_slot(32 * qb + lq, 2 * ks + hl)]);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, op[ks], s, 0, 0, 0);
+          for (int r = 0; r < 16; ++r)
+            s[qb][r] = base + (unsigned)(8 * (r >> 2) + (r & 3)) < mask_span ? s[qb][r] : -INFINITY;
         }
-        const bool need_mask = masked(t, qb);
+      }
+      bf16x8 pop[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const floatx4 l4 = *reinterpret_cast<const floatx4*>(&Ls[buf][32 * qb + 8 * a + 4 * hl]);
           floatx4 p4;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int r = 4 * a + c;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l4[c]));  // 0 on padding rows
-            if (need_mask) {
-              const int q = q0 + 8 * a + 4 * hl + c;
-              const bool ok = key_ok && (!causal || kj <= q) && (!window || kj > q - window);
-              p = ok ? p : 0.f;
-            }
-            p4[c] = p;
-          }
+          for (int c = 0; c < 4; ++c)  // 0 on padding rows (l = +inf) and masked scores
+            p4[c] = __builtin_amdgcn_exp2f(fmaf(s[qb][4 * a + c], c_log2, -l4[c]));
           Ps[pair][qb][a][lane] = p4;
           const bf16x4 pb = __builtin_convertvector(p4, bf16x4);
 #pragma unroll
           for (int c = 0; c < 4; ++c) pop[qb][a >> 1][4 * (a & 1) + c] = pb[c];  // register 4a + c
         }
-      }
       __syncthreads();  // the weights are in LDS for the K-waves
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -414,6 +451,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
           for (int db = 0; db < 4; ++db)  // dV^T += dO^T P
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Gt, 2 * qb + g, db, lane), pop[qb][g], acc[db], 0, 0, 0);
+      }
+      if (it + 1 < steps && tid < kTile) {  // the previous step's readers are past its barrier
+        Ls[buf ^ 1][tid] = l_next;
+        Ds[buf ^ 1][tid] = d_next;
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -427,16 +468,16 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
       const bf16* Gt = Gs[buf];
       floatx16 dp[2];  // dP: lane holds query q0 + 8 (r/4) + 4 hl + r%4 of key kj
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if (skip(t, qb)) continue;
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 0; ks < 8; ++ks)  // both blocks' chains interleaved, as the V-wave's S
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
           const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gt[sw_slot(32 * qb + lq, 2 * ks + hl)]);
           dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, op[ks], dp[qb], 0, 0, 0);
         }
-      }
       __syncthreads();  // the V-waves' weights are in LDS
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
