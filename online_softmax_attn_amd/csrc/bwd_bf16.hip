@@ -335,24 +335,27 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
   const int t1 = (qend + kTile - 1) / kTile;
   const int nt = t1 - t0;
   const int steps = G * nt;
-  // tile fill by eight waves: wave w writes the 1 KiB slices 2w, 2w+1 of each tile
-  int src[2];
+  // Tile fill by the four K-waves (K-wave kw writes the 1 KiB slices 4 kw .. 4 kw + 3 of each
+  // tile): the V-waves' first phase is the longer one, and loads issued by all eight waves
+  // at once queue behind each other at the start of the step.
+  const int kw = w & 3;
+  int src[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 4 * (2 * w + i) + (lane >> 4);
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * (4 * kw + i) + (lane >> 4);
     const int pc = lane & 15;
     const int c = pc ^ (((r & 3) << 2) | ((r >> 2) & 3));
     src[i] = (r * kD + 8 * c) * 2;
   }
-  auto issue = [&](int it, int buf) {
+  auto issue = [&](int it, int buf) {  // K-waves only
     const int bh = bh0 + it / nt, t = t0 + it % nt;
     const size_t base = (size_t)bh * n * kD;
     const rsrc_t rq = make_rsrc(Q + base, valid_bytes);
     const rsrc_t rg = make_rsrc(dO + base, valid_bytes);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      load_lds16(rq, (lds_void*)&Qs[buf][(2 * w + i) * 512], t * kTile * kD * 2 + src[i]);
-      load_lds16(rg, (lds_void*)&Gs[buf][(2 * w + i) * 512], t * kTile * kD * 2 + src[i]);
+    for (int i = 0; i < 4; ++i) {
+      load_lds16(rq, (lds_void*)&Qs[buf][(4 * kw + i) * 512], t * kTile * kD * 2 + src[i]);
+      load_lds16(rg, (lds_void*)&Gs[buf][(4 * kw + i) * 512], t * kTile * kD * 2 + src[i]);
     }
   };
   // the tile's LSE (log2 units, +inf on padding) and D, one query per lane of wave 0: loaded
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  issue(0, 0);
+  if (!vwave) issue(0, 0);
   if (tid < kTile) {
     float l, d;
     load_ld(0, l, d);
@@ -394,10 +397,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     for (int it = 0; it < steps; ++it) {
       const int buf = it & 1;
       float l_next = 0.f, d_next = 0.f;
-      if (it + 1 < steps) {
-        issue(it + 1, buf ^ 1);
-        if (tid < kTile) load_ld(it + 1, l_next, d_next);
-      }
+      if (it + 1 < steps && tid < kTile) load_ld(it + 1, l_next, d_next);
       const int t = t0 + it % nt;
       const bf16* Qt = Qs[buf];
       const bf16* Gt = Gs[buf];
