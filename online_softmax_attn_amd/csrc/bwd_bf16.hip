@@ -478,6 +478,15 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
           const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gt[sw_slot(32 * qb + lq, 2 * ks + hl)]);
           dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, op[ks], dp[qb], 0, 0, 0);
         }
+      // dP - D while the V-waves still form the weights (this wave would otherwise wait)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds[buf][32 * qb + 8 * a + 4 * hl]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) dp[qb][4 * a + c] -= d4[c];
+        }
       __syncthreads();  // the V-waves' weights are in LDS
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -485,11 +494,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
         bf16x8 dsop[2];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds[buf][32 * qb + 8 * a + 4 * hl]);
           const floatx4 p4 = Ps[pair][qb][a][lane];
           floatx4 ds4;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) ds4[c] = p4[c] * (dp[qb][4 * a + c] - d4[c]);
+          for (int c = 0; c < 4; ++c) ds4[c] = p4[c] * dp[qb][4 * a + c];  // dS = P (dP - D)
           const bf16x4 db4 = __builtin_convertvector(ds4, bf16x4);
 #pragma unroll
           for (int c = 0; c < 4; ++c) dsop[a >> 1][4 * (a & 1) + c] = db4[c];  // register 4a + c
