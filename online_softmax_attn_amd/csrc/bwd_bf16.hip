@@ -274,7 +274,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 // weights P of its keys and hands P to its partner through LDS, while the K-wave (waves 4-7,
 // on the same SIMD) forms dP = dO V^T.  After a barrier the V-wave accumulates dV += dO^T P
 // and the K-wave dS = P (dP - D), dK += Q^T dS.  Each wave issues 32 MFMAs per step, and the
-// two waves of a SIMD cover each other's latencies.
+// two waves of a SIMD cover each other's latencies.  The K-waves, whose first phase is the
+// shorter one, issue the tile loads and subtract D from dP before the barrier.
 constexpr int kPairThreads = 512;
 __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
