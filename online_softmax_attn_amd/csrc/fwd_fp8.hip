@@ -225,6 +225,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   // compute the scores of tile t+1 (into `nxt`); then P(t) V(t) runs while the maximum of
   // tile t+1 is taken and the previous products enter acc.  K loads run two tiles ahead,
   // V loads one.
+  // Block scales of K (tiles t and t+1) and V (tile t), read one step ahead: a scalar load
+  // inside the step would make the wave wait for every LDS read in flight as well.
+  float ks_cur = 0.f, ks_nxt = 0.f, vs_cur = 0.f;
   auto step = [&](int t, Tile& cur, Tile& nxt) {
     if (t + 2 < n_tiles) issue_k(t + 2, t & 1);
     if (t + 1 < n_tiles) issue_v(t + 1, (t + 1) & 1);
@@ -235,10 +238,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
       const float f = __builtin_amdgcn_exp2f(m_use - __builtin_fmaxf(m_ref, -1e30f));
       intx8 pop;
       if (do_next) compute_s(nxt, Ks[(t + 1) & 1]);
-      weights(cur, c_q * ks_row[t], m_use, pop);
+      weights(cur, c_q * ks_cur, m_use, pop);
       // P.V in two halves of 64 dimensions (keeps 32 product registers live), the row sum
       // of the rounded weights, and the next tile's mask and maximum in between
-      const float fv = f * vs_row[t];
+      const float fv = f * vs_cur;
       floatx16 lsum;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
           lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pop, zero16, 0, 0, 0, 0, 0, 0);
           if (do_next) {
             if (need_mask(t + 1)) apply_mask(nxt, (t + 1) * kBN);
-            m_cur = __builtin_fmaxf(m_cur, row_max(nxt, c_q * ks_row[t + 1]));
+            m_cur = __builtin_fmaxf(m_cur, row_max(nxt, c_q * ks_nxt));
           }
         }
 #pragma unroll
@@ -263,7 +266,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
       }
       l_acc = fmaf(lsum[0], f, l_acc);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the next tiles has landed
+    ks_cur = ks_nxt;
+    ks_nxt = ks_row[min(t + 2, n_blocks - 1)];
+    vs_cur = vs_row[min(t + 1, n_blocks - 1)];
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the next tiles (and scales) landed
     __syncthreads();
   };
 
@@ -277,6 +283,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   compute_s(ta, Ks[0]);
   if (need_mask(0)) apply_mask(ta, 0);
   m_cur = row_max(ta, c_q * ks_row[0]);
+  ks_cur = ks_row[0];
+  ks_nxt = ks_row[min(1, n_blocks - 1)];
+  vs_cur = vs_row[0];
   __syncthreads();  // every wave is done with K(0) before K(2) overwrites its buffer
 
   for (int t = 0; t < n_tiles; t += 2) {
