@@ -93,9 +93,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 Vs[2][kTileElems];
 
   const int HB = H * B;
-  const GridSlot slot = causal_grid_slot((int)blockIdx.x, HB, n_qtiles);
-  const int qt = n_qtiles - 1 - slot.rank;  // the last query tile has the most causal work
-  const int bh = slot.bh;
+  int qt, bh;
+  if constexpr (kWindow) {  // windows: every full tile has the same work; original order
+    qt = n_qtiles - 1 - (int)(blockIdx.x / HB);
+    const int j = blockIdx.x % HB;
+    bh = (HB % 8 == 0) ? (j % 8) * (HB / 8) + j / 8 : j;
+  } else {
+    const GridSlot slot = causal_grid_slot((int)blockIdx.x, HB, n_qtiles);
+    qt = n_qtiles - 1 - slot.rank;  // the last query tile has the most causal work
+    bh = slot.bh;
+  }
   const int b = bh / H;
   int L = lens ? lens[b] : n;
   L = L < 0 ? 0 : (L > n ? n : L);
@@ -197,14 +204,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       }
   };
   auto apply_mask = [&](Tile& T, int k0) {  // key of (kb, r) is k0 + 32 kb + 8 (r/4) + 4 hl + r%4
+    if constexpr (kWindow) {
+      // with a window (always causal) the key is admitted iff key < L and 0 <= qi - key <
+      // window: one unsigned compare plus the length test; o = key - k0 - 4 hl
+      const unsigned base = (unsigned)(qi - k0 - 4 * hl);
+      const int o_lim = L - k0 - 4 * hl;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool ok = key < L && (!causal || key <= qi) && (!kWindow || key > qi - window);
-        T.s[kb][r] = ok ? T.s[kb][r] : -INFINITY;
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
+          const bool ok = base - (unsigned)o < (unsigned)window && o < o_lim;
+          T.s[kb][r] = ok ? T.s[kb][r] : -INFINITY;
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const bool ok = key < L && (!causal || key <= qi);
+          T.s[kb][r] = ok ? T.s[kb][r] : -INFINITY;
+        }
+    }
   };
   auto need_mask = [&](int t) {
     const int k0 = t * kBN;
