@@ -84,6 +84,57 @@ def test_bf16_grouped_window(B, H, Hkv, n, causal, window, lens):
         assert np.abs(o - want).max() <= 2.0 ** -8 * np.abs(want).max()
 
 
+def _sampled_rows(H, n, fixed, per_head, seed):
+    """[H, len(fixed) + per_head]: per head the fixed positions plus `per_head` distinct
+    seeded random others, sorted."""
+    g = torch.Generator().manual_seed(seed)
+    fixed = np.asarray(fixed)
+    rows = []
+    for _ in range(H):
+        r = torch.randperm(n, generator=g).numpy()
+        r = r[~np.isin(r, fixed)][:per_head]
+        rows.append(np.sort(np.concatenate([fixed, r])))
+    return np.stack(rows)
+
+
+@pytest.mark.slow
+def test_bf16_window_workload_sampled_rows():
+    """The causal window-1024 prefill [1,32,16384,128] as it is timed (seed 6): the GPU on all
+    rows; the oracle on sampled rows of every head, among them rows before the window fills
+    (i < 1024), on both sides of the window edge and of tile edges, and the last row."""
+    q, k, v = workloads.prefill(1, 32, 16384, 128, seed=6)
+    print("case: window-1024 prefill [1,32,16384,128], sampled rows", flush=True)
+    o, lse = gpu_fwd(q, k, v, causal=True, window=1024)
+    fixed = [0, 1, 63, 64, 127, 128, 1022, 1023, 1024, 1025, 1087, 1088, 8191, 8192, 16383]
+    rows = _sampled_rows(32, 16384, fixed, 33, seed=66)
+    ro, rl = oracle.attention_rows(q, k, v, rows, causal=True, window=1024)
+    got = np.stack([o[0, h, rows[h]] for h in range(32)])[None]
+    mx, mean = errs(got, ro)
+    print(f"sampled rows max-abs {mx:.5f} mean-abs {mean:.2e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    got_l = np.stack([lse[0, h, rows[h]] for h in range(32)])[None]
+    np.testing.assert_allclose(got_l, rl, rtol=0, atol=BF16_LSE_ATOL)
+
+
+@pytest.mark.slow
+def test_bf16_grouped_workload_sampled_rows():
+    """The grouped-heads causal prefill [4,32,2048,128] with 8 K/V heads as it is timed
+    (seed 3): the GPU on all rows; the oracle on 32 rows of every (batch, head), tile edges
+    and the last row among them."""
+    q, k, v = workloads.prefill(4, 32, 2048, 128, seed=3, kv_heads=8)
+    print("case: grouped prefill [4,32,2048,128] H_kv=8, sampled rows", flush=True)
+    o, lse = gpu_fwd(q, k, v, causal=True)
+    fixed = [0, 63, 64, 127, 128, 1023, 1024, 2047]
+    rows = np.stack([_sampled_rows(32, 2048, fixed, 24, seed=67 + b) for b in range(4)])
+    ro, rl = oracle.attention_rows(q, k, v, rows, causal=True)
+    got = np.stack([np.stack([o[b, h, rows[b, h]] for h in range(32)]) for b in range(4)])
+    mx, mean = errs(got, ro)
+    print(f"sampled rows max-abs {mx:.5f} mean-abs {mean:.2e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    got_l = np.stack([np.stack([lse[b, h, rows[b, h]] for h in range(32)]) for b in range(4)])
+    np.testing.assert_allclose(got_l, rl, rtol=0, atol=BF16_LSE_ATOL)
+
+
 def test_bf16_window_equals_causal_when_longer_than_sequence():
     q, k, v = workloads.prefill(2, 4, 777, 128, seed=61, kv_heads=2)
     a, la = gpu_fwd(q, k, v, causal=True, window=777)
