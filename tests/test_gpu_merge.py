@@ -107,3 +107,38 @@ def test_chunked_causal_prefill_matches_oracle(dtype, d, chunks):
             mx, mean = errs(o, ref_o, rows)
             assert mx <= BF16_MAX and mean <= BF16_MEAN, (i, mx, mean)
             np.testing.assert_allclose(lse, ref_l, rtol=0, atol=BF16_LSE_ATOL)
+
+
+@pytest.mark.slow
+def test_sequence_parallel_share_at_full_size():
+    """Device 0's share of the long-context workload [1,32,32768,128] cut into 16 chunks of
+    2048 for 8 devices (query chunks 0 and 15, as the sequence-parallel bench times it): each
+    chunk's attention against the key chunks up to it, merged, checked on sampled rows of
+    both chunks (the chunk's first and last rows among them) against the oracle's causal
+    attention over the whole sequence."""
+    w = workloads.long_prefill()
+    q, k, v = w["q"].cuda(), w["k"].cuda(), w["v"].cuda()
+    c = 2048
+    g = torch.Generator().manual_seed(81)
+    for i in (0, 15):
+        print(f"case: sequence-parallel share, query chunk {i} of 16", flush=True)
+        qi = q[:, :, i * c:(i + 1) * c].contiguous()
+        outs, lses = [], []
+        for j in range(i + 1):
+            kj = k[:, :, j * c:(j + 1) * c].contiguous()
+            vj = v[:, :, j * c:(j + 1) * c].contiguous()
+            o, l = attn.attn_fwd(qi, kj, vj, causal=(j == i), return_lse=True)
+            outs.append(o)
+            lses.append(l)
+        o, lse = attn.attn_merge(torch.stack(outs), torch.stack(lses), return_lse=True)
+        torch.cuda.synchronize()
+        o, lse = to64(o), to64(lse)
+        rows = np.stack([np.sort(np.concatenate([[0, c - 1], torch.randperm(c - 2, generator=g)[:14].numpy() + 1]))
+                         for _ in range(32)]) + i * c
+        ro, rl = oracle.attention_rows(w["q"], w["k"], w["v"], rows, causal=True)
+        got = np.stack([o[0, h, rows[h] - i * c] for h in range(32)])[None]
+        mx, mean = errs(got, ro)
+        print(f"sampled rows max-abs {mx:.5f} mean-abs {mean:.2e}")
+        assert mx <= BF16_MAX and mean <= BF16_MEAN, (i, mx, mean)
+        got_l = np.stack([lse[0, h, rows[h] - i * c] for h in range(32)])[None]
+        np.testing.assert_allclose(got_l, rl, rtol=0, atol=BF16_LSE_ATOL)
