@@ -34,6 +34,11 @@ constexpr int kBlock = 16;
 #define ATTN_DECODE_DEPTH 2
 #endif
 constexpr int kDepth = ATTN_DECODE_DEPTH;  // blocks requested ahead of the one being consumed
+// A wave serving four or more query heads keeps one block ahead: with two, its registers
+// (the heads' accumulators and queries plus three load buffers) pass 256 and only one wave
+// fits per SIMD; with one it needs 203 and two waves share each SIMD (measured on the
+// grouped decode workload, 8 K/V heads of 4 query heads: 9% faster).
+template <int GQ> constexpr int depth_for() { return GQ >= 4 ? 1 : kDepth; }
 
 struct Partials {  // workspace views; index p = (b * H + h) * max_splits + split
   float* m;        // running max, log2 units
@@ -196,20 +201,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   };
 
   // software pipeline: kDepth + 1 register buffers, loads kDepth blocks ahead
-  Block buf[kDepth + 1];
+  constexpr int kDep = depth_for<GQ>();
+  Block buf[kDep + 1];
 #pragma unroll
-  for (int j = 0; j < kDepth; ++j)
+  for (int j = 0; j < kDep; ++j)
     if (j < count) fetch(j, buf[j]);
   int j = 0;
-  for (; j + kDepth + 1 <= count; j += kDepth + 1) {
+  for (; j + kDep + 1 <= count; j += kDep + 1) {
 #pragma unroll
-    for (int r = 0; r <= kDepth; ++r) {
-      if (j + r + kDepth < count) fetch(j + r + kDepth, buf[(r + kDepth) % (kDepth + 1)]);
+    for (int r = 0; r <= kDep; ++r) {
+      if (j + r + kDep < count) fetch(j + r + kDep, buf[(r + kDep) % (kDep + 1)]);
       consume(j + r, buf[r]);
     }
   }
 #pragma unroll
-  for (int r = 0; r <= kDepth; ++r)
+  for (int r = 0; r <= kDep; ++r)
     if (j + r < count) consume(j + r, buf[r]);
 
   const Partials P = partial_views(ws, n_part);
