@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -83,6 +83,32 @@ attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void*
                      float* lse, const int32_t* seq_lens, int batch, int heads, int kv_heads,
                      int seq_len, int head_dim, int causal, int window, float scale,
                      void* stream);
+
+/*
+ * attn_fwd_chunk — prefill attention of a contiguous chunk of queries against a longer key
+ * sequence: the q_len query rows are positions q_start .. q_start + q_len - 1 of a sequence
+ * whose kv_len keys and values are k and v, and the causal mask and window count those
+ * positions (maeste.it: future keys are set to -inf before the softmax).  This is the
+ * per-device step of sequence-parallel attention once the K/V shards are gathered (the
+ * maeste.it page leaves contexts past one GPU to sequence parallelism over several), and a
+ * prefill chunk against a cached prefix; each query block is independent work, as in the
+ * query-outer loop of pierluigilucio.it ("I Due Pilastri di FlashAttention", FA2).
+ *
+ * q, o       : [batch, heads, q_len, 128] bf16, contiguous; o written in full.
+ * k, v       : [batch, kv_heads, kv_len, 128] bf16, contiguous.
+ * lse        : optional fp32 [batch, heads, q_len], as in attn_fwd.
+ * causal     : nonzero => query row i admits keys j <= q_start + i.
+ * window     : 0, or w > 0 with causal: row i admits keys q_start + i - w < j <= q_start + i.
+ * Errors     : ATTN_ERR_INVALID for null q/k/v/o, sizes <= 0, q_start < 0,
+ *              q_start + q_len > kv_len, kv_heads <= 0 or not dividing heads, window < 0 or
+ *              without causal, scale not finite or <= 0; ATTN_ERR_UNSUPPORTED for a dtype
+ *              other than ATTN_BF16, head_dim != 128, or sizes past the 32-bit offsets.
+ * With q_start = 0 and q_len = kv_len it computes what attn_fwd computes (no seq_lens).
+ */
+attn_status attn_fwd_chunk(attn_dtype dtype, const void* q, const void* k, const void* v,
+                           void* o, float* lse, int batch, int heads, int kv_heads, int q_len,
+                           int kv_len, int q_start, int head_dim, int causal, int window,
+                           float scale, void* stream);
 
 /*
  * attn_bwd_workspace_bytes — device bytes attn_bwd needs as `workspace` (one fp32 per query

@@ -2,6 +2,7 @@
 
 Entry points mirror the C ABI in include/attn.h:
     attn_fwd                      prefill over [B, H, n, d] (fp32 or bf16), causal/length masks
+    attn_fwd_chunk                a chunk of queries at an offset into a longer key sequence
     attn_bwd                      gradients dq, dk, dv by recomputation from the saved lse
     attn_bwd_workspace_bytes      workspace size the backward pass needs
     attn_decode_paged             one query per sequence against a paged bf16 K/V cache
@@ -23,6 +24,7 @@ from .binding import (
     attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_fwd,
+    attn_fwd_chunk,
     attn_fwd_fp8,
     attn_merge,
     attn_quantize_fp8,
@@ -41,6 +43,7 @@ __all__ = [
     "attn_decode_paged",
     "attn_decode_workspace_bytes",
     "attn_fwd",
+    "attn_fwd_chunk",
     "attn_fwd_fp8",
     "attn_merge",
     "attn_quantize_fp8",

@@ -27,6 +27,8 @@ _I = ctypes.c_int
 SIGNATURES = {
     "attn_fwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                       _P]),
+    "attn_fwd_chunk": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                            ctypes.c_float, _P]),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "attn_bwd": (
         _I,
@@ -171,6 +173,44 @@ def attn_fwd(q, k, v, *, causal=False, window=0, scale=None, seq_lens=None, out=
                         _stream(stream))
     if st != ATTN_OK:
         raise AttnError("attn_fwd", st)
+    return (out, lse) if return_lse else out
+
+
+def attn_fwd_chunk(q, k, v, q_start, *, causal=False, window=0, scale=None, out=None,
+                   lse=None, return_lse=False, stream=None):
+    """A chunk of queries against a longer key sequence (bf16, d = 128): q [B, H, n_q, d] are
+    positions q_start .. q_start + n_q - 1 of the sequence whose keys and values are
+    k, v [B, H_kv, n_kv, d]; the causal mask and the window count those positions.
+    Returns o, or (o, lse) with return_lse."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, torch.bfloat16)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, H, n_q, d]; k and v one shape [B, H_kv, n_kv, d]")
+    B, H, n_q, d = q.shape
+    Hkv, n_kv = int(k.shape[1]), int(k.shape[2])
+    if k.shape[0] != B or k.shape[3] != d or Hkv < 1 or H % Hkv:
+        raise ValueError("k, v must be [B, H_kv, n_kv, d] with H a multiple of H_kv")
+    if not 0 <= int(q_start) <= n_kv - n_q:
+        raise ValueError("the chunk must lie inside the key sequence: 0 <= q_start <= n_kv - n_q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev("out", out, torch.bfloat16)
+    if out.shape != q.shape:
+        raise ValueError("out must be [B, H, n_q, d]")
+    if lse is None and return_lse:
+        lse = torch.empty(B, H, n_q, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if lse.shape != (B, H, n_q):
+            raise ValueError("lse must be [B, H, n_q]")
+    st = lib().attn_fwd_chunk(ATTN_BF16, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                              B, H, Hkv, n_q, n_kv, int(q_start), d, int(bool(causal)),
+                              int(window), float(scale), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError("attn_fwd_chunk", st)
     return (out, lse) if return_lse else out
 
 

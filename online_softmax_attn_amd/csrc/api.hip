@@ -69,10 +69,30 @@ attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void*
     if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
     return launch_status(launch_fwd_bf16(static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                                          static_cast<const bf16*>(v), static_cast<bf16*>(o), lse,
-                                         seq_lens, batch, heads, kv_heads, seq_len, causal != 0,
-                                         window, scale, s));
+                                         seq_lens, batch, heads, kv_heads, seq_len, seq_len, 0,
+                                         causal != 0, window, scale, s));
   }
   return ATTN_ERR_UNSUPPORTED;
+}
+
+attn_status attn_fwd_chunk(attn_dtype dtype, const void* q, const void* k, const void* v,
+                           void* o, float* lse, int batch, int heads, int kv_heads, int q_len,
+                           int kv_len, int q_start, int head_dim, int causal, int window,
+                           float scale, void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID;
+  if (batch <= 0 || heads <= 0 || q_len <= 0 || kv_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID;
+  if (q_start < 0 || (long long)q_start + q_len > kv_len) return ATTN_ERR_INVALID;
+  if (!heads_window_ok(heads, kv_heads, window) || (window > 0 && !causal)) return ATTN_ERR_INVALID;
+  if (!finite_positive(scale)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  // 32-bit byte offsets inside one (batch, head) slice
+  if ((long long)kv_len * head_dim * 2 >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)batch * heads * ((q_len + 127) / 128) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  return launch_status(launch_fwd_bf16(static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                                       static_cast<const bf16*>(v), static_cast<bf16*>(o), lse,
+                                       nullptr, batch, heads, kv_heads, q_len, kv_len, q_start,
+                                       causal != 0, window, scale,
+                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t attn_bwd_workspace_bytes(int batch, int heads, int seq_len) {

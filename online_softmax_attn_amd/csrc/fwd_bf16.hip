@@ -88,7 +88,11 @@ template <bool kWindow>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ lens, int B,
-    int H, int Hkv, int n, int n_qtiles, int causal, int window, float c_log2) {
+    int H, int Hkv, int n, int n_kv, int q_start, int n_qtiles, int causal, int window,
+    float c_log2) {
+  // Q, O, LSE hold n query rows; K, V hold n_kv key rows.  Query row r sits at position
+  // q_start + r of the key sequence (the causal mask and the window count positions); the
+  // plain call has n_kv = n and q_start = 0.  Lengths (lens) apply to plain calls only.
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][kTileElems];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[2][kTileElems];
 
@@ -104,20 +108,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     bh = slot.bh;
   }
   const int b = bh / H;
-  int L = lens ? lens[b] : n;
-  L = L < 0 ? 0 : (L > n ? n : L);
+  int L = lens ? lens[b] : n_kv;  // keys (and, in plain calls, queries) past L are padding
+  L = L < 0 ? 0 : (L > n_kv ? n_kv : L);
   const size_t base = (size_t)bh * n * kD;
-  const size_t kv_base = ((size_t)b * Hkv + (bh % H) / (H / Hkv)) * n * kD;
-  const int m0 = qt * kBM;
+  const size_t kv_base = ((size_t)b * Hkv + (bh % H) / (H / Hkv)) * n_kv * kD;
+  const int m0 = qt * kBM;      // first query row of the tile
+  const int p0 = q_start + m0;  // its position
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int hl = lane >> 5;    // which half of the wave
   const int lq = lane & 31;    // query column within the wave's 32
-  const int qi = m0 + w * 32 + lq;
+  const int qi = p0 + w * 32 + lq;  // this lane's query position
 
-  if (m0 >= L) {  // the whole tile is padding: o = 0, lse = -inf
+  if (p0 >= L) {  // the whole tile is padding: o = 0, lse = -inf
     for (int i = tid; i < kBM * kD / 8; i += kThreads) {
       const int r = m0 + (i * 8) / kD;
       if (r < n) *reinterpret_cast<bf16x8*>(O + base + (size_t)r * kD + (i * 8) % kD) = zero8();
@@ -129,19 +134,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // rows >= L read as zeros through the descriptors' range
   const uint32_t valid_bytes = (uint32_t)L * kD * 2;
-  const rsrc_t rq = make_rsrc(Q + base, valid_bytes);
+  const rsrc_t rq = make_rsrc(Q + base, (uint32_t)(min(L - q_start, n)) * kD * 2);
   const rsrc_t rk = make_rsrc(K + kv_base, valid_bytes);
   const rsrc_t rv = make_rsrc(V + kv_base, valid_bytes);
 
   // Q^T operand: lane (query lq, half hl) holds dims 16*ks + 8*hl .. +7 for ks = 0..7.
   bf16x8 qop[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qop[ks] = load_b128(rq, (qi * kD + 16 * ks + 8 * hl) * 2);
+  for (int ks = 0; ks < 8; ++ks)
+    qop[ks] = load_b128(rq, ((qi - q_start) * kD + 16 * ks + 8 * hl) * 2);
 
-  const int kend = causal ? min(L, m0 + kBM) : L;
+  const int kend = causal ? min(L, p0 + kBM) : L;
   const int n_tiles = (kend + kBN - 1) / kBN;                 // tiles [t_first, n_tiles)
-  const int t_first = kWindow ? max(0, m0 - window + 1) / kBN : 0;
-  const int wave_q_first = m0 + w * 32;
+  const int t_first = kWindow ? max(0, p0 - window + 1) / kBN : 0;
+  const int wave_q_first = p0 + w * 32;
   const int wave_q_last = wave_q_first + 31;
   // tiles a wave takes part in (causal: none strictly above its diagonal)
   const int wave_tiles = causal ? min(n_tiles, wave_q_last / kBN + 1) : n_tiles;
@@ -382,24 +388,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int row = m0 + w * 32 + r;
     if (row < n) *reinterpret_cast<bf16x8*>(O + base + (size_t)row * kD + 8 * c) = y;
   }
-  if (LSE && hl == 0 && qi < n)
-    LSE[(size_t)bh * n + qi] = valid ? (m_ref * ATTN_LN2 + __logf(l_tot)) : -INFINITY;
+  if (LSE && hl == 0 && qi - q_start < n)
+    LSE[(size_t)bh * n + (qi - q_start)] = valid ? (m_ref * ATTN_LN2 + __logf(l_tot)) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* lse,
                            const int32_t* seq_lens, int batch, int heads, int kv_heads, int n,
-                           int causal, int window, float scale, hipStream_t stream) {
+                           int n_kv, int q_start, int causal, int window, float scale,
+                           hipStream_t stream) {
   const int n_qtiles = (n + kBM - 1) / kBM;
   const dim3 grid((unsigned)n_qtiles * batch * heads);
   if (window > 0)
     hipLaunchKernelGGL(fwd_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, q, k, v, o, lse,
-                       seq_lens, batch, heads, kv_heads, n, n_qtiles, causal, window,
-                       scale * ATTN_LOG2E);
+                       seq_lens, batch, heads, kv_heads, n, n_kv, q_start, n_qtiles, causal,
+                       window, scale * ATTN_LOG2E);
   else
     hipLaunchKernelGGL(fwd_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, q, k, v, o, lse,
-                       seq_lens, batch, heads, kv_heads, n, n_qtiles, causal, 0,
+                       seq_lens, batch, heads, kv_heads, n, n_kv, q_start, n_qtiles, causal, 0,
                        scale * ATTN_LOG2E);
   return hipGetLastError();
 }

@@ -25,6 +25,10 @@ Functions and their pins (tests/test_oracle.py):
   online_softmax_scalar / merge / summarize / blocked_softmax
       pinned by the worked example's step table (and its wrong variant), the block-merge
       experiment design of el-ai.com section 4, and merge associativity/commutativity.
+  attention_chunk
+      pinned by the rows q_start .. of attention over the whole sequence (a square-mask
+      computation) for causal, windowed and unmasked chunks, grouped heads, and the whole
+      sequence as one chunk; by a 50-digit brute force of a tiny offset chunk.
   merge_outputs
       pinned by attention over the union of disjoint key sets (plain and causal, key sets
       of uneven size and scores up to ~+-1000), the causal decomposition of a sequence into
@@ -45,7 +49,7 @@ No function here is "parity unpinned".
 """
 
 from . import fp8
-from .attention import attend, attention, attention_rows, decode, to_f64
+from .attention import attend, attention, attention_chunk, attention_rows, decode, to_f64
 from .backward import attention_grad
 from .online import blocked_softmax, merge, merge_outputs, online_softmax_scalar, summarize
 
@@ -53,6 +57,7 @@ __all__ = [
     "fp8",
     "attend",
     "attention",
+    "attention_chunk",
     "attention_rows",
     "decode",
     "to_f64",

@@ -116,6 +116,37 @@ def attention(q, k, v, *, scale: float | None = None, causal: bool = False, seq_
     return O, LSE
 
 
+def attention_chunk(q, k, v, q_start: int, *, scale: float | None = None, causal: bool = False,
+                    window: int = 0):
+    """Attention of a chunk of queries at positions q_start .. q_start + n_q - 1 of a key
+    sequence: q [B, H, n_q, d]; k, v [B, H_kv, n_kv, d].  The causal mask (maeste.it: future
+    keys set to -inf) and the window compare key positions with those query positions.
+    Returns (O [B, H, n_q, d] fp64, LSE [B, H, n_q] fp64).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    B, H, nq, d = q.shape
+    nk = k.shape[2]
+    if not 0 <= q_start <= nk - nq:
+        raise ValueError("the chunk must lie inside the key sequence")
+    G = _group(H, k.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    pos = q_start + np.arange(nq)[:, None]
+    kj = np.arange(nk)[None, :]
+    valid = np.ones((nq, nk), dtype=bool)
+    if causal:
+        valid &= kj <= pos
+    if window:
+        valid &= kj > pos - window
+    O = np.zeros((B, H, nq, v.shape[-1]))
+    LSE = np.full((B, H, nq), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            S = scale * (q[b, h] @ k[b, h // G].T)
+            O[b, h], LSE[b, h] = attend(S, v[b, h // G], valid)
+    return O, LSE
+
+
 def attention_rows(q, k, v, rows, *, scale: float | None = None, causal: bool = False, seq_lens=None,
                    window: int = 0):
     """Attention for selected query rows only (the sampled check of long sequences).

@@ -191,3 +191,26 @@ def mg(**kw):
 ])
 def test_merge_validation(kw, status):
     assert mg(**kw) == status
+
+
+def ch(**kw):
+    a = dict(dt=attn.ATTN_BF16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=4, Hkv=2,
+             nq=100, nkv=300, q0=200, d=128, causal=1, window=0, scale=0.1)
+    a.update(kw)
+    return attn.lib().attn_fwd_chunk(a["dt"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                     a["H"], a["Hkv"], a["nq"], a["nkv"], a["q0"], a["d"],
+                                     a["causal"], a["window"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(o=None), INVALID), (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(nq=0), INVALID),
+    (dict(nkv=0), INVALID), (dict(d=0), INVALID), (dict(q0=-1), INVALID),
+    (dict(q0=201), INVALID), (dict(nq=301, q0=0), INVALID), (dict(Hkv=0), INVALID),
+    (dict(H=4, Hkv=3), INVALID), (dict(window=-1), INVALID), (dict(window=8, causal=0), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(dt=attn.ATTN_F32), UNSUPPORTED), (dict(dt=7), UNSUPPORTED), (dict(d=64), UNSUPPORTED),
+    (dict(nkv=1 << 24, nq=16, q0=0), UNSUPPORTED),
+])
+def test_fwd_chunk_validation(kw, status):
+    assert ch(**kw) == status

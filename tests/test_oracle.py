@@ -115,6 +115,47 @@ def test_attention_against_mpmath_brute_force(case):
                     assert LSE[b, h, i] == -math.inf
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_attention_chunk_against_mpmath(case):
+    """A chunk of queries at an offset into the key sequence: the causal mask and the window
+    compare key positions with the chunk's query positions q_start + i."""
+    rng = np.random.default_rng(2500 + case)
+    H, Hkv, nk, d = 4, 2, 9, 3
+    nq = int(rng.integers(1, nk + 1))
+    q_start = int(rng.integers(0, nk - nq + 1))
+    causal = case % 3 != 0
+    window = 3 if case % 3 == 2 else 0
+    q = rng.normal(size=(1, H, nq, d)) * 5
+    k = rng.normal(size=(1, Hkv, nk, d)) * 5
+    v = rng.normal(size=(1, Hkv, nk, d))
+    O, LSE = oracle.attention_chunk(q, k, v, q_start, causal=causal, window=window)
+    for h in range(H):
+        for i in range(nq):
+            p = q_start + i
+            admitted = [j for j in range(nk) if (not causal or j <= p) and (not window or j > p - window)]
+            want, want_lse = _mp_attention_row(q[0, h, i], k[0, h // 2], v[0, h // 2], 1 / math.sqrt(d), admitted)
+            np.testing.assert_allclose(O[0, h, i], want, rtol=1e-13, atol=1e-14)
+            assert abs(LSE[0, h, i] - want_lse) <= 1e-13 * max(1.0, abs(want_lse))
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 37)])
+def test_attention_chunk_is_the_rows_of_whole_sequence_attention(causal, window):
+    """Chunk i of a sequence equals rows q_start .. of attention over the whole sequence
+    (the square-mask computation), for every chunk of an uneven cut; the whole sequence as
+    one chunk is plain attention."""
+    rng = np.random.default_rng(2600 + window + int(causal))
+    B, H, Hkv, n, d = 2, 4, 2, 150, 8
+    q = rng.normal(size=(B, H, n, d)) * 3
+    k = rng.normal(size=(B, Hkv, n, d)) * 3
+    v = rng.normal(size=(B, Hkv, n, d))
+    ro, rl = oracle.attention(q, k, v, causal=causal, window=window)
+    cuts = [0, 1, 40, 64, 129, 150]
+    for a, c in zip(cuts[:-1], cuts[1:]):
+        o, l = oracle.attention_chunk(q[:, :, a:c], k, v, a, causal=causal, window=window)
+        np.testing.assert_allclose(o, ro[:, :, a:c], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l, rl[:, :, a:c], rtol=1e-14, atol=1e-13)
+
+
 @pytest.mark.parametrize("case", range(4))
 def test_attention_rows_against_mpmath(case):
     rng = np.random.default_rng(2000 + case)
