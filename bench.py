@@ -35,8 +35,11 @@ oracle timed on this host over a bounded sample of the prefill workload.
                   roofline is the dense fp8 MFMA peak.
 --workload cp     one device's share of sequence-parallel causal attention over the
                   [1, 32, 32768, 128] workload: 16 chunks for 8 devices (zig-zag), device 0's
-                  17 chunk pairs through attn_fwd and their two attn_merge calls (the K/V
-                  exchange between devices is not part of it).
+                  two query chunks, each one attn_fwd_chunk against the gathered K/V (the
+                  K/V exchange between devices is not part of it).
+--workload cp-ring
+                  the same share as a ring delivers K/V chunks one at a time: device 0's 17
+                  chunk pairs through attn_fwd and their two attn_merge calls.
 --profile-pass    runs one 1 GiB device copy, one prefill and one decode and exits (the
                   command the rocprofv3 counter and trace runs wrap).
 --record-traffic FETCH_CSV WRITE_CSV
@@ -297,10 +300,13 @@ def bench_cp(args):
     """One device's share of sequence-parallel causal attention over the long-context workload.
 
     [1, 32, 32768, 128] cut into 2G = 16 chunks of 2048 tokens for G = 8 devices, device g
-    owning query chunks g and 2G-1-g (zig-zag: every device gets 17 chunk pairs).  For an
-    owned chunk c the share is attn_fwd of Q_c against K/V chunks 0..c (no mask off the
-    diagonal, causal on it) and one attn_merge of those c+1 results.  All chunks are
-    resident on this one GPU: the exchange of K/V chunks between devices is not part of it.
+    owning query chunks g and 2G-1-g (zig-zag: every device gets 17 chunk pairs of causal
+    work).  `--workload cp`: the K/V shards gathered first (an all-gather over the node's
+    direct links), the share is one attn_fwd_chunk per owned query chunk against the whole
+    K/V (the causal mask stops it at the chunk's last position).  `--workload cp-ring`: the
+    form that consumes K/V chunks one at a time as a ring delivers them: attn_fwd of the
+    query chunk against each K/V chunk (causal on the diagonal one) and one attn_merge of
+    the c+1 results.  All data is resident on this one GPU: the exchange itself is not timed.
     """
     import torch
 
@@ -316,20 +322,27 @@ def bench_cp(args):
     c = n // C
     chunk = lambda t, j: t[:, :, j * c:(j + 1) * c].contiguous()
     owned = [g_dev, C - 1 - g_dev]
+    ring = args.workload == "cp-ring"
     Qc = {i: chunk(q, i) for i in owned}
-    Kc = [chunk(k, j) for j in range(max(owned) + 1)]
-    Vc = [chunk(v, j) for j in range(max(owned) + 1)]
-    del q, k, v
-    parts = {i: torch.empty(i + 1, B, H, c, d, dtype=torch.bfloat16, device=dev) for i in owned}
-    lses = {i: torch.empty(i + 1, B, H, c, dtype=torch.float32, device=dev) for i in owned}
     outs = {i: torch.empty(B, H, c, d, dtype=torch.bfloat16, device=dev) for i in owned}
     out_lse = {i: torch.empty(B, H, c, dtype=torch.float32, device=dev) for i in owned}
+    if ring:
+        Kc = [chunk(k, j) for j in range(max(owned) + 1)]
+        Vc = [chunk(v, j) for j in range(max(owned) + 1)]
+        del k, v
+        parts = {i: torch.empty(i + 1, B, H, c, d, dtype=torch.bfloat16, device=dev) for i in owned}
+        lses = {i: torch.empty(i + 1, B, H, c, dtype=torch.float32, device=dev) for i in owned}
+    del q
 
     def step():
         for i in owned:
-            for j in range(i + 1):
-                attn.attn_fwd(Qc[i], Kc[j], Vc[j], causal=(j == i), out=parts[i][j], lse=lses[i][j])
-            attn.attn_merge(parts[i], lses[i], out=outs[i], lse=out_lse[i])
+            if ring:
+                for j in range(i + 1):
+                    attn.attn_fwd(Qc[i], Kc[j], Vc[j], causal=(j == i), out=parts[i][j],
+                                  lse=lses[i][j])
+                attn.attn_merge(parts[i], lses[i], out=outs[i], lse=out_lse[i])
+            else:
+                attn.attn_fwd_chunk(Qc[i], k, v, i * c, causal=True, out=outs[i], lse=out_lse[i])
 
     for _ in range(args.warmup):
         step()
@@ -349,6 +362,9 @@ def bench_cp(args):
     n_full = sum(owned)
     flops = n_full * full + len(owned) * diag
     tf = flops / (ms * 1e-3) / 1e12
+    form = (f"{n_full} unmasked + {len(owned)} causal chunk pairs + {len(owned)} merges, K/V "
+            f"chunks as a ring delivers them" if ring else
+            f"one chunk launch per owned query chunk against the gathered K/V")
     print(json.dumps({
         "metric": "sequence-parallel causal attention: one device's share, TFLOPS",
         "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -356,9 +372,8 @@ def bench_cp(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V of the long-context workload)",
         "config": {"workload": f"causal prefill B=1 H=32 n=32768 d=128 in {C} chunks of {c} for "
-                               f"{G} devices (zig-zag); device {g_dev}: query chunks {owned}, "
-                               f"{n_full} unmasked + {len(owned)} causal chunk pairs + "
-                               f"{len(owned)} merges; K/V exchange not included"},
+                               f"{G} devices (zig-zag); device {g_dev}: query chunks {owned}; "
+                               f"{form}; the K/V exchange itself not included"},
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
         "ms_avg": round(ms, 5)}))
@@ -375,7 +390,8 @@ def main():
     # right after 5 warm-up steps runs ~15% slower than the same burst 30 ms later), so the
     # default warm-up keeps the GPU busy for ~60 ms before anything is timed.
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", choices=["prefill", "long", "backward", "grouped", "window", "fp8", "cp"],
+    ap.add_argument("--workload", choices=["prefill", "long", "backward", "grouped", "window", "fp8", "cp",
+                                           "cp-ring"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -400,7 +416,7 @@ def main():
         return bench_backward(args)
     if args.workload == "fp8":
         return bench_fp8(args)
-    if args.workload == "cp":
+    if args.workload in ("cp", "cp-ring"):
         return bench_cp(args)
     window, kv_heads = 0, 32
     dec_cfg = " + paged decode B=32 H=32 d=128 lens U[1024,8192] block 16"
