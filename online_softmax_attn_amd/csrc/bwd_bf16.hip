@@ -10,8 +10,8 @@
 //     dV_j = sum_i P_ij dO_i            dP_ij = <dO_i, v_j>
 //     dS_ij = P_ij (dP_ij - D_i)        dQ_i = scale sum_j dS_ij k_j
 //                                       dK_j = scale sum_i dS_ij q_i
-// Three kernels: D (a row reduction), dQ (one wave per 32 queries, sweeping key tiles, as
-// the forward pass does) and dK/dV (a pair of waves per 32 keys, sweeping query tiles: one
+// Two kernels: dQ (one wave per 32 queries, sweeping key tiles, as the forward pass does;
+// it also forms D_i from the dO row it holds and leaves it for the next kernel) and dK/dV (a pair of waves per 32 keys, sweeping query tiles: one
 // wave forms the weights and dV, its partner dP, dS and dK, with the weights handed over
 // through LDS).  Both sweeps use the forward's register layouts: the MFMA column is the row
 // that owns the accumulator (a query for dQ, a key for dK/dV), weights go from the score
@@ -39,11 +39,6 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 // 8 rows of one transposed read spread over all four 64-byte bank groups.
 __device__ __forceinline__ int sw_slot(int r, int c) {
   return r * kD + ((c ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 3);
-}
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int n) {
@@ -83,42 +78,12 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int g, int db, in
   return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// ------------------------------------------------------------------------ D = <dO_i, O_i>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restrict__ O,
-                                                           const bf16* __restrict__ dO,
-                                                           float* __restrict__ Dv,
-                                                           const int32_t* __restrict__ lens,
-                                                           int H, int n, long long rows) {
-  const long long row = ((long long)blockIdx.x * kThreads + threadIdx.x) >> 4;  // 16 lanes per row
-  const int part = threadIdx.x & 15;
-  const bool live = row < rows;
-  float x = 0.f;
-  if (live) {
-    const uint4 o = *reinterpret_cast<const uint4*>(O + row * kD + 8 * part);
-    const uint4 g = *reinterpret_cast<const uint4*>(dO + row * kD + 8 * part);
-    const uint32_t* ow = reinterpret_cast<const uint32_t*>(&o);
-    const uint32_t* gw = reinterpret_cast<const uint32_t*>(&g);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ow[e]), __builtin_bit_cast(bf16x2, gw[e]), x, false);
-  }
-  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp<0x141>(x);  // row_half_mirror
-  x += dpp<0x140>(x);  // row_mirror
-  if (live && part == 0) {
-    const long long bh = row / n;
-    const int i = (int)(row % n);
-    const int L = clamp_len(lens, (int)(bh / H), n);
-    Dv[row] = i < L ? x : 0.f;
-  }
-}
-
 // ------------------------------------------------------------------------ dQ
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    const int32_t* __restrict__ lens, float* __restrict__ dQ, int B, int H, int Hkv, int n,
+    const bf16* __restrict__ dO, const bf16* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ Dv, const int32_t* __restrict__ lens, float* __restrict__ dQ, int B,
+    int H, int Hkv, int n,
     int n_qtiles, int causal, int window, float c_log2, float scale) {
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][kTileElems];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[2][kTileElems];
@@ -140,6 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       const int r = m0 + (i * 4) / kD;
       if (r < n) *reinterpret_cast<floatx4*>(dQ + base + (size_t)r * kD + (i * 4) % kD) = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+    for (int r = m0 + tid; r < min(m0 + kBM, n); r += kThreads) Dv[(size_t)bh * n + r] = 0.f;
     return;
   }
 
@@ -161,7 +127,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   // (else -n) and hi = window when one is set (else n); a padding query admits none
   const int mask_lo = causal ? 0 : -n;
   const int mask_hi = window ? window : n;
-  const float Di = row_ok ? Dv[(size_t)bh * n + qi] : 0.f;
+  // D_i = <dO_i, O_i>: this lane holds half of row qi of dO (the operand above); O is read in
+  // the same layout and the halves of lanes l and l ^ 32 are added.  Written for the dK/dV
+  // kernel (0 on padding rows).
+  float Di;
+  {
+    const rsrc_t ro = make_rsrc(O + base, valid_bytes);
+    float x = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 ov = load_b128(ro, (qi * kD + 16 * ks + 8 * hl) * 2);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        x = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{ov[e], ov[e + 1]}, bf16x2{gop[ks][e], gop[ks][e + 1]}, x, false);
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    Di = row_ok ? __uint_as_float(sw[0]) + __uint_as_float(sw[1]) : 0.f;
+    if (hl == 0 && qi < n) Dv[(size_t)bh * n + qi] = Di;
+  }
 
   const int kend = causal ? min(L, m0 + kBM) : L;
   const int n_tiles = (kend + kTile - 1) / kTile;  // tiles [t_first, n_tiles); tile t in buffer t & 1
@@ -540,19 +523,13 @@ hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf
                            float* dq, float* dk, float* dv, int batch, int heads, int kv_heads,
                            int n, int causal, int window, float scale, void* workspace,
                            hipStream_t stream) {
-  float* Dv = static_cast<float*>(workspace);
-  const long long rows = (long long)batch * heads * n;
-  const unsigned pre_blocks = (unsigned)((rows * 16 + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3(pre_blocks), dim3(kThreads), 0, stream, o, dout, Dv,
-                     seq_lens, heads, n, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  float* Dv = static_cast<float*>(workspace);  // D_i per query row, written by the dQ kernel
   const float c_log2 = scale * ATTN_LOG2E;
   const int n_qtiles = (n + 127) / 128;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)n_qtiles * batch * heads), dim3(kThreads), 0,
-                     stream, q, k, v, dout, lse, Dv, seq_lens, dq, batch, heads, kv_heads, n,
+                     stream, q, k, v, dout, o, lse, Dv, seq_lens, dq, batch, heads, kv_heads, n,
                      n_qtiles, causal, window, c_log2, scale);
-  e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_ktiles = (n + 127) / 128;
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)n_ktiles * batch * kv_heads), dim3(kPairThreads),
