@@ -87,3 +87,25 @@ def test_backward_deterministic():
     _, b = run(1, 2, 300, True, None, seed=31)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_backward_workspace_contents_unused():
+    """The workspace is scratch: what it holds before the call (zero bytes, then NaN bytes)
+    never reaches the gradients, also with padding rows and query tiles wholly past a
+    sequence's end (length 40 of 300 leaves two of its three 128-row tiles empty)."""
+    B, H, n, lens = 2, 2, 300, [300, 40]
+    print(f"case: bwd workspace poison B={B} H={H} n={n} lens={lens}", flush=True)
+    q, k, v = workloads.prefill(B, H, n, 128, seed=41, lens=lens, poison=True)
+    g = torch.Generator().manual_seed(42)
+    do = torch.randn(B, H, n, 128, generator=g).to(torch.bfloat16).cuda()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o, lse = attn.attn_fwd(qd, kd, vd, causal=True, seq_lens=lens, return_lse=True)
+    need = attn.attn_bwd_workspace_bytes(B, H, n)
+    outs = []
+    for fill in (0, 0xFF):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        outs.append(attn.attn_bwd(qd, kd, vd, o, do, lse, causal=True, seq_lens=lens, workspace=ws))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert bool(torch.isfinite(a).all())
+        assert torch.equal(a, b)
