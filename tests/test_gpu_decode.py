@@ -65,3 +65,26 @@ def test_decode_split_invariance():
         assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
     for o in outs[1:]:
         assert np.abs(o - outs[0]).max() <= 2 * 2.0 ** -8  # a couple of bf16 ulps at |o| < 1
+
+
+@pytest.mark.parametrize("kv_heads,window", [(None, 0), (2, 300)])
+def test_decode_workspace_contents_unused(kv_heads, window):
+    """The split workspace is scratch: what it holds before the call (zero bytes, then NaN
+    bytes) never reaches the output, also where most splits of the grid lie past a short
+    sequence's end (lengths 1 and 20 beside 3000)."""
+    lens = [3000, 1, 20, 1500]
+    w = workloads.paged(lens, 8, 128, seed=61, kv_heads=kv_heads, poison=True)
+    print(f"case: decode workspace poison lens={lens} kv_heads={kv_heads} window={window}", flush=True)
+    q, kc, vc, bt = w.q.cuda(), w.k_cache.cuda(), w.v_cache.cuda(), w.block_table.cuda()
+    need = attn.attn_decode_workspace_bytes(len(lens), 8, 128, w.max_seq_len, 64,
+                                            kv_heads=kv_heads, window=window)
+    outs = []
+    for fill in (0, 0xFF):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        o, lse = attn.attn_decode_paged(q, kc, vc, bt, lens, max_seq_len=w.max_seq_len,
+                                        window=window, kv_split=64, workspace=ws, return_lse=True)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert bool(torch.isfinite(a).all())
+        assert torch.equal(a, b)
