@@ -51,6 +51,21 @@ for (B, H, Hkv, n, causal) in [(32, 32, 32, 512, True), (16, 32, 32, 1024, True)
     print(f"| [{B},{H},{n},128] kv_heads {Hkv} {'causal' if causal else 'full'} | {ms*1e3:.1f} µs | {tf:.1f} | {tf/PEAK*100:.1f}% |", flush=True)
     del q, k, v, o
 
+print("== fp32 (fp64 scores)", flush=True)
+for (B, H, n, d, causal, lens) in [(1, 1, 256, 64, False, None), (4, 4, 1000, 64, True, [1000, 900, 500, 17]),
+                                   (4, 32, 2048, 128, True, None)]:
+    gf = torch.Generator(device=dev).manual_seed(1)
+    q, k, v = (torch.randn(B, H, n, d, generator=gf, device=dev) for _ in range(3))
+    o = torch.empty_like(q)
+    ms = timed(lambda: attn.attn_fwd(q, k, v, causal=causal, seq_lens=lens, out=o))
+    if lens is None:
+        pairs = B * (n * (n + 1) / 2 if causal else n * n)
+    else:
+        pairs = sum(L * (L + 1) / 2 if causal else L * L for L in lens)
+    tf = 4 * d * H * pairs / ms / 1e9
+    print(f"| fp32 [{B},{H},{n},{d}] {'causal' if causal else 'full'}{' lens ' + str(lens) if lens else ''} | {ms*1e3:.1f} µs | {tf:.2f} | {tf/78.6*100:.1f}% of fp64 |", flush=True)
+    del q, k, v, o
+
 print("== fp8", flush=True)
 for (B, H, n, causal) in [(4, 32, 2048, True), (1, 32, 8192, True), (4, 32, 4096, False)]:
     q, k, v = qkv(B, H, H, n)
