@@ -74,3 +74,33 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+def test_summarize_trace_averages_exactly_the_timed_launches(tmp_path, capsys):
+    # launch order: 3 untimed prefills, then K = 2 timed ones; long and decode likewise
+    rows, t = [], 0
+    def add(name, grid, dur):
+        nonlocal t
+        rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur,
+                     "Grid_Size_X": grid, "Grid_Size_Y": 1, "Grid_Size_Z": 1})
+        t += dur + 10
+    for dur in (900, 800, 700, 150_000, 170_000):           # ns; the last two are timed
+        add("void fwd_bf16_kernel<false>(...)", 2048 * 256, dur)
+    for dur in (9_000_000, 8_000_000, 8_200_000):          # first long launch is untimed
+        add("void fwd_bf16_kernel<false>(...)", 8192 * 256, dur)
+    for dur in (400_000, 380_000, 390_000):
+        add("void decode_split_kernel<1>(...)", 32 * 32 * 16 * 64, dur)
+        add("void decode_merge_kernel(...)", 32 * 32 * 64, 5_000)
+    with open(tmp_path / "trace.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=list(rows[0]))
+        wr.writeheader()
+        wr.writerows(rows)
+    line = {"metric": "m", "steps": 2, "prefill": {"ms_avg": 0.16}, "long_prefill": {"ms_avg": 8.1},
+            "decode": {"ms_avg": 0.39},
+            "trace_index": {"prefill_first": 3, "long_first": 1, "decode_first": 1}}
+    (tmp_path / "line.log").write_text("noise\n" + json.dumps(line) + "\n")
+    bench.summarize_trace(str(tmp_path / "trace.csv"), str(tmp_path / "line.log"))
+    out = capsys.readouterr().out
+    assert "| 160.00 | 160.00 |" in out          # (150 + 170) / 2 us, line 0.16 ms
+    assert "| 8100.00 | 8100.00 |" in out        # (8000 + 8200) / 2 us
+    assert "| 390.00 |" in out                   # decode split + merge: (380+390)/2 + 5
