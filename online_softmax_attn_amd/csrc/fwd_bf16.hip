@@ -28,11 +28,14 @@
 //   * exp is v_exp_f32 (2^x): scores are scaled by scale*log2(e) inside one FMA.
 //   * the normaliser sums the bf16-ROUNDED weights that enter the P.V product (dot2 with
 //     ones), so rounding of P cancels in u/l to first order.
-//   * causal: tiles strictly above a wave's diagonal are skipped; every query tile of one
-//     (batch, head) lands on the same XCD, eight heads at a time, heaviest tiles first
-//     (causal_grid_slot), so K/V are re-read from that XCD's L2.  Consecutive heads share an
-//     XCD, so the query heads of one K/V group (grouped heads) read their shared K/V from
-//     one L2 as well.
+//   * causal: the key loop ends at the workgroup's diagonal; a wave whose own diagonal lies
+//     a tile earlier scores that last tile along with the others but skips its weights and
+//     P.V (one straight-line step for all waves keeps the loop free of per-wave branches,
+//     and the compiler interleaves the weights' FMAs and exps with the score products).
+//     Every query tile of one (batch, head) lands on the same XCD, eight heads at a time,
+//     heaviest tiles first (causal_grid_slot), so K/V are re-read from that XCD's L2.
+//     Consecutive heads share an XCD, so the query heads of one K/V group (grouped heads)
+//     read their shared K/V from one L2 as well.
 //   * causal window w: the key loop starts at the first tile any query of the workgroup
 //     admits (query i admits keys i - w < j <= i); tiles that cross a window edge are
 //     masked like the diagonal ones.
@@ -49,6 +52,7 @@ constexpr int kTileElems = kBN * kD;
 constexpr float kSlack = 8.0f;  // log2 headroom of the lazily raised reference maximum
 
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) char lds_char;
 
 // LDS element offset of logical 16-byte chunk `c` (0..15) of row `r` in a K tile: the chunk
 // index is XORed with r % 16, so the 16 rows one MFMA operand read touches hit 16 distinct
@@ -133,10 +137,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   }
 
   // rows >= L read as zeros through the descriptors' range
-  const uint32_t valid_bytes = (uint32_t)L * kD * 2;
   const rsrc_t rq = make_rsrc(Q + base, (uint32_t)(min(L - q_start, n)) * kD * 2);
-  const rsrc_t rk = make_rsrc(K + kv_base, valid_bytes);
-  const rsrc_t rv = make_rsrc(V + kv_base, valid_bytes);
 
   // Q^T operand: lane (query lq, half hl) holds dims 16*ks + 8*hl .. +7 for ks = 0..7.
   bf16x8 qop[8];
@@ -154,7 +155,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // Direct global->LDS tile fill: wave w fills 1 KiB slices 4w..4w+3 of each tile; lane i of
   // slice j lands in row 4j + i/16, physical chunk i%16, so it fetches the logical chunk the
-  // swizzle puts there.
+  // swizzle puts there.  Each tile is read through a descriptor whose base is the tile's
+  // first row and whose range ends at row L, so the per-lane offsets are loop invariants
+  // and rows past L still read as zeros.
   int k_src[4], v_src[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -163,15 +166,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     k_src[i] = (r * kD + 8 * (pc ^ (r & 15))) * 2;
     v_src[i] = (r * kD + 8 * (pc ^ ((r & 3) << 2))) * 2;
   }
-  auto issue_k = [&](int t, int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      load_lds16(rk, (lds_void*)&Ks[buf][(4 * w + i) * 512], t * kBN * kD * 2 + k_src[i]);
+  const bf16* k_head = K + kv_base;
+  const bf16* v_head = V + kv_base;
+  auto tile_rsrc = [&](const bf16* head, int t) __attribute__((always_inline)) {
+    const int first = t * kBN;
+    return make_rsrc(head + (size_t)first * kD, (uint32_t)max(L - first, 0) * kD * 2);
   };
-  auto issue_v = [&](int t, int buf) {
+  // this wave's 4 KiB slice of a tile, as a wave-uniform (scalar) LDS byte offset
+  const int lds_w = __builtin_amdgcn_readfirstlane(w * 4 * 512 * 2);
+  auto lds_dst = [&](bf16* tile, int i) __attribute__((always_inline)) {
+    return (lds_void*)((lds_char*)(lds_void*)tile + lds_w + i * 1024);
+  };
+  auto issue_k = [&](int t, int buf) __attribute__((always_inline)) {
+    const rsrc_t r = tile_rsrc(k_head, t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      load_lds16(rv, (lds_void*)&Vs[buf][(4 * w + i) * 512], t * kBN * kD * 2 + v_src[i]);
+    for (int i = 0; i < 4; ++i) load_lds16(r, lds_dst(Ks[buf], i), k_src[i]);
+  };
+  auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
+    const rsrc_t r = tile_rsrc(v_head, t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_lds16(r, lds_dst(Vs[buf], i), v_src[i]);
   };
 
   floatx16 acc[4];  // O^T, d blocks of 32: lane holds d = 32*db + 8*(r/4) + 4*hl + r%4
@@ -183,9 +197,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // maximum lazily: it is raised (and l, u rescaled by 2^(old - new)) only when some score
   // of the wave exceeds it by more than kSlack, so weights stay <= 2^kSlack and the
   // rescale — exact in real arithmetic whichever reference is used — is mostly skipped.
+  // Whether a tile needs a raise is read off the weights' own row sum: a lane whose sum is
+  // at most 2^kSlack has no weight above it, so only a larger (or infinite) sum leads to
+  // the tile's exact row maximum, the reference raised to it and a second evaluation of
+  // the weights.  No row maximum is taken on the common path.
   float m_ref = -INFINITY;
   float m_use = -1e30f;  // m_ref floored: no -inf - (-inf) on rows with no key yet
   float l_run = 0.f;     // this lane's half of the normaliser
+  constexpr float kSumLimit = 256.0f;  // 2^kSlack
 
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
@@ -195,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int tr_col = 16 * (g & 1) + 4 * (s & 3);           // + 32*db
 
   // ---- building blocks ----------------------------------------------------------------
-  auto compute_s = [&](Tile& T, const bf16* Kt) {  // S^T = K Q^T, 16 MFMA + 16 LDS reads
+  auto compute_s = [&](Tile& T, const bf16* Kt) __attribute__((always_inline)) {  // S^T = K Q^T, 16 MFMA + 16 LDS reads
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -209,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         T.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], T.s[kb], 0, 0, 0);
       }
   };
-  auto apply_mask = [&](Tile& T, int k0) {  // key of (kb, r) is k0 + 32 kb + 8 (r/4) + 4 hl + r%4
+  auto apply_mask = [&](Tile& T, int k0) __attribute__((always_inline)) {  // key of (kb, r) is k0 + 32 kb + 8 (r/4) + 4 hl + r%4
     if constexpr (kWindow) {
       // with a window (always causal) the key is admitted iff key < L and 0 <= qi - key <
       // window: one unsigned compare plus the length test; o = key - k0 - 4 hl
@@ -224,22 +243,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           T.s[kb][r] = ok ? T.s[kb][r] : -INFINITY;
         }
     } else {
+      // admitted iff key < min(L, qi + 1) (causal) or key < L: one compare per score
+      const int lim = (causal ? min(L, qi + 1) : L) - k0 - 4 * hl;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool ok = key < L && (!causal || key <= qi);
-          T.s[kb][r] = ok ? T.s[kb][r] : -INFINITY;
+          const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
+          T.s[kb][r] = o < lim ? T.s[kb][r] : -INFINITY;
         }
     }
   };
-  auto need_mask = [&](int t) {
+  auto need_mask = [&](int t) __attribute__((always_inline)) {  // wave-uniform
     const int k0 = t * kBN;
     return (k0 + kBN > L) || (causal && k0 + kBN - 1 > wave_q_first) ||
            (kWindow && k0 <= wave_q_last - window);
   };
-  auto row_max = [&](const Tile& T) {  // scaled (log2 units) max over this tile's 64 keys
+  auto row_max = [&](const Tile& T) __attribute__((always_inline)) {  // scaled (log2 units) max over this tile's 64 keys
     float mx = __builtin_fmaxf(T.s[0][0], T.s[0][1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, T.s[0][r]), T.s[0][r + 1]);
@@ -247,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, T.s[1][r]), T.s[1][r + 1]);
     return other_half_max(mx) * c_log2;
   };
-  auto raise_ref = [&](float mx) {  // the lazy rescale of l and u
+  auto raise_ref = [&](float mx) __attribute__((always_inline)) {  // the lazy rescale of l and u
     if (__any(mx > m_ref + kSlack)) {
       // floor at -1e30: a lane with no admitted key yet gets alpha = 0, never NaN
       const float m_new = __builtin_fmaxf(__builtin_fmaxf(m_ref, mx), -1e30f);
@@ -261,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
     m_use = __builtin_fmaxf(m_ref, -1e30f);
   };
-  auto weights = [&](const Tile& T, bf16x8 (&pop)[4]) {  // P^T operand, returns its row sum
+  auto weights = [&](const Tile& T, bf16x8 (&pop)[4]) __attribute__((always_inline)) {  // P^T operand, returns its row sum
     float psum = 0.f;
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
@@ -279,7 +299,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
     return psum;
   };
-  auto pv = [&](const bf16* Vt, const bf16x8 (&pop)[4]) {  // O^T += V^T P^T
+  // The raise check on the weights of tile T (see m_ref): the common case costs one compare.
+  // A lane whose row sum exceeds 2^kSlack (or is infinite) sends the wave to the exact row
+  // maximum; the reference rises to it (alpha = 1 on lanes it does not move) and the
+  // weights are evaluated again, now each at most 1.
+  auto checked_weights = [&](const Tile& T, bf16x8 (&pop)[4], float psum) __attribute__((always_inline)) {
+    if (__builtin_expect(__any(!(psum <= kSumLimit) && psum == psum), 0)) {
+      const float m_new = __builtin_fmaxf(__builtin_fmaxf(m_ref, row_max(T)), -1e30f);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 from the empty state
+      m_ref = m_new;
+      m_use = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      psum = weights(T, pop);
+    }
+    l_run += psum;
+  };
+  auto pv = [&](const bf16* Vt, const bf16x8 (&pop)[4]) __attribute__((always_inline)) {  // O^T += V^T P^T
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp)
 #pragma unroll
@@ -298,53 +337,50 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
 
   // One pipelined step: the weights of tile t (in `cur`) are formed while the matrix cores
-  // compute the scores of tile t+1 (into `nxt`); then P(t) V(t) is accumulated while the
-  // row maximum of tile t+1 is taken.  Loads run two tiles ahead for K, one for V.
-  auto step = [&](int t, Tile& cur, Tile& nxt) {
-    const bool has_next = t + 1 < n_tiles;
+  // compute the scores of tile t+1 (into `nxt`); then P(t) V(t) is accumulated.  Loads run
+  // two tiles ahead for K, one for V.  Every wave of the workgroup runs these steps up to
+  // the workgroup's last tile, so the step is one straight block and the weights' FMAs and
+  // exps interleave with the score products; a wave whose diagonal lies before the last
+  // tile scores that tile needlessly but never uses it (step_last skips it).
+  const int t_last = n_tiles - 1;
+  auto step = [&](int t, Tile& cur, Tile& nxt) __attribute__((always_inline)) {
     if (t + 2 < n_tiles) issue_k(t + 2, t & 1);
-    if (has_next) issue_v(t + 1, (t + 1) & 1);
-    if (t < wave_tiles) {
-      const bool do_next = t + 1 < wave_tiles;
-      bf16x8 pop[4];
-      float psum;
-      if (do_next) {
-        compute_s(nxt, Ks[(t + 1) & 1]);
-        psum = weights(cur, pop);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+    issue_v(t + 1, (t + 1) & 1);
+    bf16x8 pop[4];
+    compute_s(nxt, Ks[(t + 1) & 1]);
+    const float psum = weights(cur, pop);
+    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 6, 0);
-          if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-        }
-      } else {
-        psum = weights(cur, pop);
-      }
-      l_run += psum;
-      if (do_next && need_mask(t + 1)) apply_mask(nxt, (t + 1) * kBN);
-      float mx = 0.f;
-      if (do_next) {
-        pv(Vs[t & 1], pop);
-        mx = row_max(nxt);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 8, 1);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 1, 1);
-          if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 1);
-        }
-        raise_ref(mx);
-      } else {
-        pv(Vs[t & 1], pop);
-      }
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVALU, 6, 0);
+      if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
     }
+    checked_weights(cur, pop, psum);
+    pv(Vs[t & 1], pop);
+    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 8, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 1);
+      if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 1);
+    }
+    // tile t+1 is used unless it is the last tile and lies past this wave's diagonal
+    if ((t + 1 < wave_tiles || t + 1 < t_last) && need_mask(t + 1)) apply_mask(nxt, (t + 1) * kBN);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the next tiles has landed
     __syncthreads();
   };
+  // The last tile: its weights and P V, no loads, no barrier after it (its K tile was read in
+  // the step before, whose barrier frees the K buffers for the epilogue).
+  auto step_last = [&](int t, Tile& cur) __attribute__((always_inline)) {
+    if (t < wave_tiles) {
+      bf16x8 pop[4];
+      checked_weights(cur, pop, weights(cur, pop));
+      pv(Vs[t & 1], pop);
+    }
+  };
 
   // ---- prologue: K(t0), V(t0), K(t0+1) in flight; scores and max of tile t0.  Tile t
-  // always lives in buffer t & 1.
+  // always lives in buffer t & 1, its scores in ta when t - t0 is even, else in tb.
   const int t0 = t_first;
   issue_k(t0, t0 & 1);
   issue_v(t0, t0 & 1);
@@ -357,10 +393,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   raise_ref(row_max(ta));
   __syncthreads();  // every wave is done with K(t0) before K(t0+2) overwrites its buffer
 
-  for (int t = t0; t < n_tiles; t += 2) {
+  for (int t = t0; t < t_last; t += 2) {
     step(t, ta, tb);
-    if (t + 1 < n_tiles) step(t + 1, tb, ta);
+    if (t + 1 < t_last) step(t + 1, tb, ta);
   }
+  if (((t_last - t0) & 1) == 0)
+    step_last(t_last, ta);
+  else
+    step_last(t_last, tb);
 
   // ---- epilogue: o = u / l, staged through LDS so that each store instruction writes four
   // whole 256-byte rows of O.  Every wave has passed the last step's barrier, so the K
