@@ -34,6 +34,11 @@ Functions and their pins (tests/test_oracle.py):
       of uneven size and scores up to ~+-1000), the causal decomposition of a sequence into
       query/key chunks, part-order invariance, empty parts, and the closed form for two
       parts of equal LSE (mean of the outputs, LSE + ln 2).
+  attention_grad_magnitudes (backward.py)
+      pinned by the triangle inequality against the gradients (every magnitude at least
+      the gradient element), its equality cases (dO >= 0 gives |dV| = dV; a single admitted
+      key gives |dV| = |dO| and |dQ|, |dK| as written out for P = 1), and by sums of
+      absolute values over an explicit loop of the terms on tiny inputs.
   attention_grad (backward.py)
       pinned by 50-digit central differences of the forward definition (masks, padding)
       (also two query heads sharing one K/V head under a causal window) and by closed forms
@@ -50,7 +55,7 @@ No function here is "parity unpinned".
 
 from . import fp8
 from .attention import attend, attention, attention_chunk, attention_rows, decode, to_f64
-from .backward import attention_grad
+from .backward import attention_grad, attention_grad_magnitudes
 from .online import blocked_softmax, merge, merge_outputs, online_softmax_scalar, summarize
 
 __all__ = [
@@ -62,6 +67,7 @@ __all__ = [
     "decode",
     "to_f64",
     "attention_grad",
+    "attention_grad_magnitudes",
     "online_softmax_scalar",
     "merge",
     "merge_outputs",

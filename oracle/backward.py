@@ -62,3 +62,41 @@ def attention_grad(q, k, v, dout, *, scale: float | None = None, causal: bool = 
             dq[b, h, :L] = scale * (dS @ K)
             dk[b, hk, :L] += scale * (dS.T @ Q)
     return dq, dk, dv
+
+
+def attention_grad_magnitudes(q, k, v, dout, *, scale: float | None = None, causal: bool = False,
+                              seq_lens=None, window: int = 0):
+    """Per-element sums of the absolute values of the terms each gradient element adds up,
+    in the decomposition written above (a tolerance scale for evaluations that round some
+    factor of every term):
+
+        |dV|_jc = sum_i P_ij |dO_ic|
+        |dQ|_ic = scale * sum_j P_ij (|dP_ij| + D+_i) |K_jc|
+        |dK|_jc = scale * sum_i P_ij (|dP_ij| + D+_i) |Q_ic|
+
+    with D+_i = sum_c |dO_ic O_ic| bounding the row term D_i = sum_k P_ik dP_ik = <dO_i, O_i>.
+    By the triangle inequality each is at least the magnitude of the gradient element it
+    belongs to.  Returns (Aq, Ak, Av) shaped like (dQ, dK, dV)."""
+    q, k, v, dout = to_f64(q), to_f64(k), to_f64(v), to_f64(dout)
+    B, H, n, d = q.shape
+    G = _group(H, k.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lens = [n] * B if seq_lens is None else [int(x) for x in seq_lens]
+    aq, ak, av = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        L = lens[b]
+        if L <= 0:
+            continue
+        valid = _valid(L, L, causal, window)
+        for h in range(H):
+            hk = h // G
+            Q, K, V, dO = q[b, h, :L], k[b, hk, :L], v[b, hk, :L], dout[b, h, :L]
+            P = _probabilities(scale * (Q @ K.T), valid)
+            O = P @ V
+            d_plus = np.abs(dO * O).sum(axis=1, keepdims=True)
+            T = P * (np.abs(dO @ V.T) + d_plus)
+            av[b, hk, :L] += P.T @ np.abs(dO)
+            aq[b, h, :L] = scale * (T @ np.abs(K))
+            ak[b, hk, :L] += scale * (T.T @ np.abs(Q))
+    return aq, ak, av

@@ -1,13 +1,14 @@
 """Parity of attn_bwd with the oracle's fp64 gradients, on seeded inputs: the GPU forward
 supplies o and lse (as in training), the GPU backward recomputes the weights from them.
 
-Tolerance (derived from the arithmetic): every gradient is a sum of products in which one
-factor carries bf16 rounding — the weight P or dS packed for the MFMA (relative 2^-9), the
-bf16 output O inside D = <dO, O> (2^-9), and the forward's log-sum-exp, whose normaliser
-summed bf16-rounded weights (2^-8).  Per term that is at most 2^-7 relative; the tests hold
-mean|err| <= 2^-7 mean|ref| and max|err| <= 2^-6 max|ref| per gradient tensor, plus an
-absolute 1e-6 for the fp32 accumulation order where the exact gradient vanishes (a single
-key sends no gradient to q or k, but D and dP are summed in different orders)."""
+Tolerance (derived from the arithmetic): every gradient element is a sum of terms in each
+of which one factor carries bf16 rounding — the weight P or dS packed for the MFMA (relative
+2^-9), the bf16 output O inside D = <dO, O> (2^-9), and the forward's log-sum-exp, whose
+normaliser summed bf16-rounded weights (2^-9).  Per term that is under 2^-7 relative, so
+each element is held to 2^-6 of the sum of the absolute values of its own terms (the
+oracle's attention_grad_magnitudes), plus an absolute 1e-6 for the fp32 accumulation order
+where the exact gradient vanishes (a single key sends no gradient to q or k, but D and dP
+are summed in different orders).  The tensor mean is held to 2^-7 of the reference mean."""
 
 import numpy as np
 import pytest
@@ -36,11 +37,15 @@ def run(B, H, n, causal, lens, seed):
     return (q, k, v, do), [to64(x) for x in grads]
 
 
-def check(got, ref, name):
+def check(got, ref, mag, name):
+    """Element-wise |err| <= 2^-6 * (sum of |terms| of that element) + 1e-6, and the mean."""
     assert np.all(np.isfinite(got)), f"{name}: non-finite"
     err = np.abs(got - ref)
+    bound = MAX_REL * mag + ATOL
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    print(f"{name}: max err/bound {float((err / bound).max()):.3f}; max err {err.max():.2e}")
+    assert np.all(err <= bound), (name, worst, err[worst], mag[worst])
     assert err.mean() <= MEAN_REL * np.abs(ref).mean() + ATOL, (name, err.mean(), np.abs(ref).mean())
-    assert err.max() <= MAX_REL * np.abs(ref).max() + ATOL, (name, err.max(), np.abs(ref).max())
 
 
 CASES = [(1, 1, 1, False, None), (1, 1, 64, False, None), (1, 2, 64, True, None),
@@ -54,8 +59,9 @@ def test_backward_shapes(B, H, n, causal, lens):
     print(f"case: bwd B={B} H={H} n={n} causal={causal} lens={lens}", flush=True)
     (q, k, v, do), got = run(B, H, n, causal, lens, seed=11 * n + B)
     ref = oracle.attention_grad(q, k, v, do, causal=causal, seq_lens=lens)
-    for name, x, r in zip(("dq", "dk", "dv"), got, ref):
-        check(x, r, name)
+    mag = oracle.attention_grad_magnitudes(q, k, v, do, causal=causal, seq_lens=lens)
+    for name, x, r, a in zip(("dq", "dk", "dv"), got, ref, mag):
+        check(x, r, a, name)
         if lens is not None:
             for b, L in enumerate(lens):
                 assert np.all(x[b, :, L:] == 0), name
@@ -68,8 +74,9 @@ def test_backward_causal_prefill_shape():
     (q, k, v, do), got = run(4, 32, 2048, True, None, seed=3)
     sl = (slice(0, 1), slice(0, 16))
     ref = oracle.attention_grad(q[sl], k[sl], v[sl], do[sl], causal=True)
-    for name, x, r in zip(("dq", "dk", "dv"), got, ref):
-        check(x[sl], r, name)
+    mag = oracle.attention_grad_magnitudes(q[sl], k[sl], v[sl], do[sl], causal=True)
+    for name, x, r, a in zip(("dq", "dk", "dv"), got, ref, mag):
+        check(x[sl], r, a, name)
 
 
 def test_backward_closed_forms():

@@ -128,3 +128,69 @@ def test_zero_queries_give_zero_key_gradient_and_single_key_rows():
     dq1, dk1, dv1 = oracle.attention_grad(q + 1.0, k, v, do, seq_lens=[1])
     np.testing.assert_array_equal(dv1[0, 0, 0], do[0, 0, 0])
     assert np.all(dq1 == 0) and np.all(dk1 == 0)
+
+
+# ------------------------------------------------------------------ term magnitudes
+def _terms_loop(q, k, v, do, scale, causal):
+    """|terms| of each gradient element by explicit loops over (i, j, c) on one head."""
+    n, d = q.shape
+    S = np.array([[scale * sum(q[i, c] * k[j, c] for c in range(d)) for j in range(n)] for i in range(n)])
+    ok = np.array([[(not causal) or j <= i for j in range(n)] for i in range(n)])
+    P = np.zeros((n, n))
+    for i in range(n):
+        w = [math.exp(S[i, j]) if ok[i, j] else 0.0 for j in range(n)]
+        P[i] = np.array(w) / sum(w)
+    O = P @ v
+    aq, ak, av = np.zeros((n, d)), np.zeros((n, d)), np.zeros((n, d))
+    for i in range(n):
+        dplus = sum(abs(do[i, c] * O[i, c]) for c in range(d))
+        for j in range(n):
+            dp = sum(do[i, c] * v[j, c] for c in range(d))
+            t = P[i, j] * (abs(dp) + dplus)
+            for c in range(d):
+                av[j, c] += P[i, j] * abs(do[i, c])
+                aq[i, c] += scale * t * abs(k[j, c])
+                ak[j, c] += scale * t * abs(q[i, c])
+    return aq, ak, av
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_magnitudes_against_explicit_term_loops(causal):
+    rng = np.random.default_rng(17 + causal)
+    q, k, v, do = (rng.normal(size=(5, 3)) for _ in range(4))
+    got = oracle.attention_grad_magnitudes(q[None, None], k[None, None], v[None, None],
+                                           do[None, None], causal=causal)
+    want = _terms_loop(q, k, v, do, 1 / math.sqrt(3), causal)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g[0, 0], w, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal,lens,window,hkv", [(False, None, 0, 2), (True, [9, 4], 0, 1),
+                                                    (True, None, 3, 2)])
+def test_gradient_magnitudes_bound_the_gradients(causal, lens, window, hkv):
+    rng = np.random.default_rng(5)
+    q, do = (rng.normal(size=(2, 2, 9, 4)) * s for s in (3.0, 1.0))
+    k, v = (rng.normal(size=(2, hkv, 9, 4)) * s for s in (3.0, 1.0))
+    grads = oracle.attention_grad(q, k, v, do, causal=causal, seq_lens=lens, window=window)
+    mags = oracle.attention_grad_magnitudes(q, k, v, do, causal=causal, seq_lens=lens, window=window)
+    for g, a in zip(grads, mags):
+        assert g.shape == a.shape
+        assert np.all(np.abs(g) <= a * (1 + 1e-12) + 1e-15)
+
+
+def test_gradient_magnitudes_equality_cases():
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.normal(size=(1, 1, 6, 4)) for _ in range(3))
+    do = np.abs(rng.normal(size=(1, 1, 6, 4)))           # dO >= 0: dV has no cancellation
+    _, _, dv = oracle.attention_grad(q, k, v, do)
+    _, _, av = oracle.attention_grad_magnitudes(q, k, v, do)
+    np.testing.assert_allclose(av, dv, rtol=1e-13)
+    # one admitted key per row (causal row 0): |dV|_0 gets |dO_0| from row 0 alone
+    q1, k1, v1, do1 = (rng.normal(size=(1, 1, 1, 4)) for _ in range(4))
+    aq, ak, av = oracle.attention_grad_magnitudes(q1, k1, v1, do1, causal=True)
+    np.testing.assert_allclose(av[0, 0, 0], np.abs(do1[0, 0, 0]), rtol=1e-15)
+    # P = 1, dP = <dO, V>, D+ = sum |dO * V|: |dQ| = scale (|<dO,V>| + D+) |K|
+    dp = float(do1[0, 0, 0] @ v1[0, 0, 0])
+    dplus = float(np.abs(do1[0, 0, 0] * v1[0, 0, 0]).sum())
+    np.testing.assert_allclose(aq[0, 0, 0], 0.5 * (abs(dp) + dplus) * np.abs(k1[0, 0, 0]), rtol=1e-14)
+    np.testing.assert_allclose(ak[0, 0, 0], 0.5 * (abs(dp) + dplus) * np.abs(q1[0, 0, 0]), rtol=1e-14)
