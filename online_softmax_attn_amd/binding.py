@@ -10,6 +10,7 @@ the library is not built this module raises instead of computing anything anothe
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 
@@ -91,6 +92,24 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
+def _on_stream(fn):
+    """Run an entry point with its `stream` argument (a torch.cuda.Stream or a raw hipStream_t
+    handle) as torch's current stream, so that everything the binding allocates for the call
+    (outputs, workspaces, uploaded lengths) belongs to the stream the kernels run on: the
+    caching allocator then never hands that memory to other work while the kernels still
+    use it."""
+
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, stream=None, **kwargs)
+        ts = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(ts):
+            return fn(*args, stream=ts, **kwargs)
+
+    return wrapper
+
+
 def _check_dev(name, t, dtype=None):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
@@ -137,6 +156,7 @@ def _kv_heads(q, k, v):
     return Hkv
 
 
+@_on_stream
 def attn_fwd(q, k, v, *, causal=False, window=0, scale=None, seq_lens=None, out=None,
              lse=None, return_lse=False, stream=None):
     """Prefill attention: q [B, H, n, d], k and v [B, H_kv, n, d] (fp32 d in {64,128};
@@ -176,6 +196,7 @@ def attn_fwd(q, k, v, *, causal=False, window=0, scale=None, seq_lens=None, out=
     return (out, lse) if return_lse else out
 
 
+@_on_stream
 def attn_fwd_chunk(q, k, v, q_start, *, causal=False, window=0, scale=None, out=None,
                    lse=None, return_lse=False, stream=None):
     """A chunk of queries against a longer key sequence (bf16, d = 128): q [B, H, n_q, d] are
@@ -214,6 +235,7 @@ def attn_fwd_chunk(q, k, v, q_start, *, causal=False, window=0, scale=None, out=
     return (out, lse) if return_lse else out
 
 
+@_on_stream
 def attn_merge(o_parts, lse_parts, *, out=None, lse=None, return_lse=False, stream=None):
     """Attention over the union of disjoint key sets from each set's (o, lse).
 
@@ -252,6 +274,7 @@ def attn_bwd_workspace_bytes(batch, heads, seq_len) -> int:
     return int(lib().attn_bwd_workspace_bytes(batch, heads, seq_len))
 
 
+@_on_stream
 def attn_bwd(q, k, v, o, dout, lse, *, causal=False, window=0, scale=None, seq_lens=None,
              dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Gradients (dq, dk, dv) in fp32 of sum(o * dout), recomputing the weights from lse.
@@ -302,6 +325,7 @@ def attn_decode_workspace_bytes(batch, heads, head_dim, max_seq_len, kv_split=0,
                                                  window, kv_split))
 
 
+@_on_stream
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, window=0,
                       scale=None, kv_split=0, out=None, lse=None, return_lse=False,
                       workspace=None, stream=None):
@@ -327,10 +351,14 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len
     if out is None:
         out = torch.empty_like(q)
     _check_dev("out", out, torch.bfloat16)
+    if tuple(out.shape) != (B, H, d):
+        raise ValueError("out must be [B, H, d]")
     if lse is None and return_lse:
         lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_dev("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, H):
+            raise ValueError("lse must be [B, H]")
     need = attn_decode_workspace_bytes(B, H, d, max_seq_len, kv_split, kv_heads=Hkv,
                                        window=window)
     if workspace is None:
@@ -351,6 +379,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len
 FP8_BLOCK = 64  # rows per quantisation block (one fp32 scale each)
 
 
+@_on_stream
 def attn_quantize_fp8(x, *, seq_lens=None, transpose=False, out=None, scales=None, stream=None):
     """E4M3 codes (uint8) and fp32 block scales of a bf16 [B, H, n, 128] tensor.
 
@@ -381,6 +410,7 @@ def attn_quantize_fp8(x, *, seq_lens=None, transpose=False, out=None, scales=Non
     return out, scales
 
 
+@_on_stream
 def attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, *, causal=False, scale=None,
                  seq_lens=None, out=None, lse=None, return_lse=False, stream=None):
     """Prefill attention on E4M3 operands from attn_quantize_fp8 (q, k row-major, v

@@ -4,8 +4,9 @@ Follows el-ai.com "Attenzione: softmax online, riscalamento e memoria":
   * section 2: after a prefix of keys keep m (prefix maximum), l (sum of exp(s - m)) and
     u (the same sum weighted by the values).  For a new pair (s, v) the new maximum is
     m' = max(m, s); both l AND u are multiplied by exp(m - m') and only then is the new
-    key's exp(s - m') and exp(s - m') * v added.  The first key starts the state at
-    (s_1, 1, v_1), which never forms -inf - (-inf).
+    key's exp(s - m') and exp(s - m') * v added.  The recurrence here starts from the state
+    of no key at all, (m, l, u) = (-inf, 0, 0), whose carry factor is taken as 0, so the
+    first key yields the page's initial state (s_1, 1, v_1) without forming -inf - (-inf).
   * section 4: two summaries of disjoint key sets merge the same way: take the larger
     maximum, bring both normalisers and numerators to it, add.
 The output is o = u / l.  These routines are the algorithm written out step by step in
@@ -33,15 +34,15 @@ def online_softmax_scalar(scores, values, *, rescale_numerator: bool = True):
         raise ValueError("a row needs at least one admitted key")
     if any(not math.isfinite(s) for s in scores):
         raise ValueError("scores must be finite")
-    m, l, u = scores[0], 1.0, values[0].copy()
-    steps = [(m, l, u / l)]
-    for s, x in zip(scores[1:], values[1:]):
-        m_new = max(m, s)
-        old = math.exp(m - m_new)  # brings every earlier term to the new maximum
-        new = math.exp(s - m_new)
-        l = l * old + new
-        u = (u * old if rescale_numerator else u) + new * x
-        m = m_new
+    m, l, u = -math.inf, 0.0, np.zeros_like(values[0])   # no key seen yet
+    steps = []
+    for s, x in zip(scores, values):
+        m_next = max(m, s)
+        carry = 0.0 if m == -math.inf else math.exp(m - m_next)  # earlier terms, rebased
+        w = math.exp(s - m_next)                                  # the new key's weight
+        l = carry * l + w
+        u = (carry * u if rescale_numerator else u) + w * x
+        m = m_next
         steps.append((m, l, u / l))
     return u / l, steps
 

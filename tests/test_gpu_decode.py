@@ -88,3 +88,35 @@ def test_decode_workspace_contents_unused(kv_heads, window):
     for a, b in zip(*outs):
         assert bool(torch.isfinite(a).all())
         assert torch.equal(a, b)
+
+
+def test_decode_and_backward_on_a_side_stream():
+    """Entry points called with stream=<a side stream>: the binding allocates the outputs, the
+    workspaces and the uploaded lengths on that stream, so the default stream's allocations
+    made meanwhile (here filled with NaN) never take memory the side stream's kernels still
+    use.  Results match the oracle."""
+    print("case: decode and backward on a side stream", flush=True)
+    side = torch.cuda.Stream()
+    w = workloads.paged([700, 33, 1500, 4000], 4, 128, seed=78, kv_heads=2)
+    q, kc, vc, tbl = w.q.cuda(), w.k_cache.cuda(), w.v_cache.cuda(), w.block_table.cuda()
+    qp, kp, vp = workloads.prefill(1, 4, 300, 128, seed=79, kv_heads=2)
+    do = torch.randn(1, 4, 300, 128, generator=torch.Generator().manual_seed(80)).to(torch.bfloat16)
+    qpd, kpd, vpd, dod = qp.cuda(), kp.cuda(), vp.cuda(), do.cuda()
+    o_f, lse_f = attn.attn_fwd(qpd, kpd, vpd, causal=True, return_lse=True)
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        o = attn.attn_decode_paged(q, kc, vc, tbl, w.seq_lens.tolist(), max_seq_len=w.max_seq_len,
+                                   stream=side)
+        grads = attn.attn_bwd(qpd, kpd, vpd, o_f, dod, lse_f, causal=True, stream=side)
+        # default-stream traffic while the side stream runs
+        junk = [torch.full((1 << 22,), float("nan"), device="cuda") for _ in range(8)]
+        del junk
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ro, _ = oracle.decode(w.q, w.k_seqs, w.v_seqs)
+    mx, mean = errs(to64(o), ro)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    refs = oracle.attention_grad(qp, kp, vp, do, causal=True)
+    mags = oracle.attention_grad_magnitudes(qp, kp, vp, do, causal=True)
+    for g, r, a in zip(grads, refs, mags):
+        assert np.all(np.abs(to64(g) - r) <= 2.0 ** -6 * a + 1e-6)
