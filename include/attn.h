@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -191,6 +191,29 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_cac
                               int num_blocks, int max_blocks_per_seq, int max_seq_len,
                               int window, float scale, int kv_split, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_noalloc — attn_decode_paged for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without `workspace` / `workspace_bytes`, the same kernels and results.
+ * The split partials go to a device array of ATTN_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; the call allocates and frees
+ * nothing.  Its contents on entry do not matter.
+ * Errors     : those of attn_decode_paged; ATTN_ERR_WORKSPACE when
+ *              attn_decode_workspace_bytes(...) for these arguments exceeds
+ *              ATTN_NOALLOC_SCRATCH_BYTES (nothing is enqueued); ATTN_ERR_LAUNCH when the
+ *              array's device address cannot be obtained.
+ * Concurrency: calls on one GPU share its array; calls that overlap in time on one GPU (on
+ *              different streams or from different host threads) race on it — serialise
+ *              them.  Calls on different GPUs are independent.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+attn_status attn_decode_paged_noalloc(attn_dtype dtype, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_table,
+                                      const int32_t* seq_lens, void* o, float* lse, int batch,
+                                      int heads, int kv_heads, int head_dim, int block_size,
+                                      int num_blocks, int max_blocks_per_seq, int max_seq_len,
+                                      int window, float scale, int kv_split, void* stream);
 
 /*
  * attn_quantize_fp8 — block quantisation of a bf16 tensor to FP8 E4M3, the operand format of

@@ -7,6 +7,7 @@ Entry points mirror the C ABI in include/attn.h:
     attn_bwd_workspace_bytes      workspace size the backward pass needs
     attn_decode_paged             one query per sequence against a paged bf16 K/V cache
     attn_decode_workspace_bytes   workspace size the decode needs
+    attn_decode_paged_noalloc     the decode without a workspace (allocates nothing)
     attn_quantize_fp8             bf16 -> FP8 E4M3 codes with one scale per 64-row block
     attn_fwd_fp8                  prefill on E4M3 operands (bf16 output)
     attn_merge                    join results over disjoint key sets by their lse
@@ -15,13 +16,20 @@ Entry points mirror the C ABI in include/attn.h:
 
 from .binding import (
     ATTN_BF16,
+    ATTN_ERR_INVALID,
+    ATTN_ERR_LAUNCH,
+    ATTN_ERR_UNSUPPORTED,
+    ATTN_ERR_WORKSPACE,
     ATTN_F32,
+    ATTN_NOALLOC_SCRATCH_BYTES,
+    ATTN_OK,
     LIB_PATH,
     AttnError,
     attn_abi_version,
     attn_bwd,
     attn_bwd_workspace_bytes,
     attn_decode_paged,
+    attn_decode_paged_noalloc,
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_fwd_chunk,
@@ -34,13 +42,20 @@ from .binding import (
 
 __all__ = [
     "ATTN_BF16",
+    "ATTN_ERR_INVALID",
+    "ATTN_ERR_LAUNCH",
+    "ATTN_ERR_UNSUPPORTED",
+    "ATTN_ERR_WORKSPACE",
     "ATTN_F32",
+    "ATTN_NOALLOC_SCRATCH_BYTES",
+    "ATTN_OK",
     "LIB_PATH",
     "AttnError",
     "attn_abi_version",
     "attn_bwd",
     "attn_bwd_workspace_bytes",
     "attn_decode_paged",
+    "attn_decode_paged_noalloc",
     "attn_decode_workspace_bytes",
     "attn_fwd",
     "attn_fwd_chunk",

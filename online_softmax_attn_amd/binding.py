@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_LAUNCH = range(5)
 ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/attn.h: the no-alloc decode's scratch array
 
 # name -> (restype, argtypes), exactly the declarations of include/attn.h
 _P = ctypes.c_void_p
@@ -41,6 +42,11 @@ SIGNATURES = {
         _I,
         [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
          _P, ctypes.c_size_t, _P],
+    ),
+    "attn_decode_paged_noalloc": (
+        _I,
+        [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
+         _P],
     ),
     "attn_quantize_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
@@ -373,6 +379,46 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len
     if st != ATTN_OK:
         raise AttnError("attn_decode_paged", st)
     return (out, lse) if return_lse else out
+
+
+@_on_stream
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, out,
+                              window=0, scale=None, kv_split=0, lse=None, stream=None):
+    """attn_decode_paged without a workspace: the library's fixed per-GPU scratch array holds
+    the split partials (ATTN_NOALLOC_SCRATCH_BYTES; larger requests raise AttnError with
+    ATTN_ERR_WORKSPACE).  `out` (and `lse`, if wanted) must be given; `seq_lens` must be a
+    device int32 tensor, so the call allocates nothing.  Overlapping calls on one GPU race."""
+    for name, t, dt in (("q", q, torch.bfloat16), ("k_cache", k_cache, torch.bfloat16),
+                        ("v_cache", v_cache, torch.bfloat16), ("block_table", block_table, torch.int32),
+                        ("out", out, torch.bfloat16)):
+        _check_dev(name, t, dt)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, H, d]; caches [num_blocks, H_kv, block_size, d]")
+    B, H, d = q.shape
+    nb, Hkv, bs, dc = k_cache.shape
+    if Hkv < 1 or H % Hkv or dc != d:
+        raise ValueError("cache heads must divide the query heads; head_dim must match q")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    if tuple(out.shape) != (B, H, d):
+        raise ValueError("out must be [B, H, d]")
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, H):
+            raise ValueError("lse must be [B, H]")
+    if not (isinstance(seq_lens, torch.Tensor) and seq_lens.is_cuda):
+        raise ValueError("seq_lens must be a device int32 tensor (an upload would allocate)")
+    lens = _lengths(seq_lens, B, max_seq_len, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().attn_decode_paged_noalloc(
+        ATTN_BF16, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        lens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        B, H, Hkv, d, bs, nb, int(block_table.shape[1]), int(max_seq_len), int(window),
+        float(scale), int(kv_split), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError("attn_decode_paged_noalloc", st)
+    return out
 
 
 # --------------------------------------------------------------------------- FP8 E4M3

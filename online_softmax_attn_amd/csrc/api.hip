@@ -29,6 +29,28 @@ int resolve_split(int batch, int heads, int kv_heads, int max_seq_len, int windo
 
 }  // namespace
 
+attn_status decode_paged_check(attn_dtype dtype, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const void* o, int batch, int heads,
+                               int kv_heads, int head_dim, int block_size, int num_blocks,
+                               int max_blocks_per_seq, int max_seq_len, int window, float scale,
+                               int kv_split, int* split, size_t* need) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o) return ATTN_ERR_INVALID;
+  if (batch <= 0 || heads <= 0 || head_dim <= 0 || num_blocks <= 0 || max_seq_len <= 0)
+    return ATTN_ERR_INVALID;
+  if (block_size <= 0 || max_blocks_per_seq <= 0) return ATTN_ERR_INVALID;
+  if (!heads_window_ok(heads, kv_heads, window)) return ATTN_ERR_INVALID;
+  if (!finite_positive(scale)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_BF16 || head_dim != 128 || block_size != kDecodeBlock)
+    return ATTN_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size < max_seq_len) return ATTN_ERR_INVALID;
+  if (batch > 65535 || heads > 65535) return ATTN_ERR_UNSUPPORTED;  // grid.y / grid.z limits
+  *split = resolve_split(batch, heads, kv_heads, max_seq_len, window, kv_split);
+  if (*split == 0) return ATTN_ERR_INVALID;
+  *need = decode_workspace_bytes(batch, heads, head_dim, max_seq_len, window, *split);
+  return ATTN_OK;
+}
+
 extern "C" {
 
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }
@@ -184,19 +206,13 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_cac
                               int num_blocks, int max_blocks_per_seq, int max_seq_len,
                               int window, float scale, int kv_split, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o) return ATTN_ERR_INVALID;
-  if (batch <= 0 || heads <= 0 || head_dim <= 0 || num_blocks <= 0 || max_seq_len <= 0)
-    return ATTN_ERR_INVALID;
-  if (block_size <= 0 || max_blocks_per_seq <= 0) return ATTN_ERR_INVALID;
-  if (!heads_window_ok(heads, kv_heads, window)) return ATTN_ERR_INVALID;
-  if (!finite_positive(scale)) return ATTN_ERR_INVALID;
-  if (dtype != ATTN_BF16 || head_dim != 128 || block_size != kDecodeBlock)
-    return ATTN_ERR_UNSUPPORTED;
-  if ((long long)max_blocks_per_seq * block_size < max_seq_len) return ATTN_ERR_INVALID;
-  if (batch > 65535 || heads > 65535) return ATTN_ERR_UNSUPPORTED;  // grid.y / grid.z limits
-  const int split = resolve_split(batch, heads, kv_heads, max_seq_len, window, kv_split);
-  if (split == 0) return ATTN_ERR_INVALID;
-  const size_t need = decode_workspace_bytes(batch, heads, head_dim, max_seq_len, window, split);
+  int split = 0;
+  size_t need = 0;
+  const attn_status st = decode_paged_check(dtype, q, k_cache, v_cache, block_table, seq_lens,
+                                            o, batch, heads, kv_heads, head_dim, block_size,
+                                            num_blocks, max_blocks_per_seq, max_seq_len, window,
+                                            scale, kv_split, &split, &need);
+  if (st != ATTN_OK) return st;
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   return launch_status(launch_decode_paged(
       static_cast<const bf16*>(q), static_cast<const bf16*>(k_cache),

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn.h"
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -48,6 +50,15 @@ hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v
                                float* lse, int batch, int heads, int kv_heads, int num_blocks,
                                int max_blocks_per_seq, int max_seq_len, int window, float scale,
                                int split, void* workspace, hipStream_t stream);
+
+// Every host-visible check of attn_decode_paged (include/attn.h); on ATTN_OK also the split
+// length the call will use and the workspace bytes it needs.
+attn_status decode_paged_check(attn_dtype dtype, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const void* o, int batch, int heads,
+                               int kv_heads, int head_dim, int block_size, int num_blocks,
+                               int max_blocks_per_seq, int max_seq_len, int window, float scale,
+                               int kv_split, int* split, size_t* need);
 
 // Grouped-head decode on the matrix cores (partials in the layout decode_merge_kernel reads);
 // launch_decode_paged picks it for groups of 8 or more query heads per K/V head.

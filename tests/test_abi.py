@@ -214,3 +214,32 @@ def ch(**kw):
 ])
 def test_fwd_chunk_validation(kw, status):
     assert ch(**kw) == status
+
+
+def dec_noalloc(**kw):
+    a = dict(dtype=1, q=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, lens=FAKE, o=FAKE, lse=None, B=2, H=4,
+             Hkv=4, d=128, bs=16, nb=16, mb=8, msl=128, window=0, scale=0.1, split=0)
+    a.update(kw)
+    return attn.lib().attn_decode_paged_noalloc(
+        a["dtype"], a["q"], a["kc"], a["vc"], a["tbl"], a["lens"], a["o"], a["lse"], a["B"],
+        a["H"], a["Hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["msl"], a["window"], a["scale"],
+        a["split"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(lens=None), INVALID),
+    (dict(B=0), INVALID), (dict(mb=7), INVALID), (dict(split=24), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(bs=32, mb=4), UNSUPPORTED), (dict(Hkv=3), INVALID),
+    # partials past the fixed scratch array: 64 x 64 heads x 128 splits of 520 bytes
+    (dict(B=64, H=64, Hkv=64, msl=65536, mb=4096, split=512), WORKSPACE),
+])
+def test_decode_noalloc_validation(kw, status):
+    """The no-alloc decode runs every check of attn_decode_paged, and refuses partials that
+    would not fit its scratch array, before any HIP call."""
+    assert dec_noalloc(**kw) == status
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert attn.ATTN_NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
