@@ -238,7 +238,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   }
 
   if (qi < n) {
-    float* drow = dQ + base + (size_t)qi * kD;
+    // the lane's half index is taken afresh from the lane id (mbcnt) rather than kept live
+    // through the key loop, which runs at the register limit
+    const int hl_out = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
+    float* drow = dQ + base + (size_t)qi * kD + 4 * hl_out;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         floatx4 x;
 #pragma unroll
         for (int c = 0; c < 4; ++c) x[c] = row_ok ? acc[db][4 * a + c] * scale : 0.f;
-        *reinterpret_cast<floatx4*>(drow + 32 * db + 8 * a + 4 * hl) = x;
+        *reinterpret_cast<floatx4*>(drow + 32 * db + 8 * a) = x;
       }
   }
 }

@@ -305,11 +305,11 @@ int max_splits_for(int max_seq_len, int window, int split) {
 // kernel 3.0 TB/s at every group size.
 constexpr int kMfmaGroup = 8;
 
-// Query heads one wave of decode_split_kernel serves: the largest of 8, 4, 2, 1 that divides
-// the group size.
+// Query heads one wave of decode_split_kernel serves: the largest of 4, 2, 1 that divides
+// the group size (groups of kMfmaGroup or more heads never reach this kernel).
 int heads_per_wave(int heads, int kv_heads) {
   const int G = heads / kv_heads;
-  return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+  return G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
 }
 
 // waves per (sequence, split): decode_gqa_kernel takes up to 32 heads of a group per wave
@@ -369,7 +369,6 @@ hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v
                      max_blocks_per_seq, max_seq_len, window, max_splits, split / kBlock,       \
                      c_log2, n_part)
   switch (gq) {
-    case 8: ATTN_DECODE_LAUNCH(8); break;
     case 4: ATTN_DECODE_LAUNCH(4); break;
     case 2: ATTN_DECODE_LAUNCH(2); break;
     default: ATTN_DECODE_LAUNCH(1); break;
