@@ -32,6 +32,8 @@ CASES = [
     (1, 2, 2, 1, 513, 512, True, 0),       # a single query at the last position
     (1, 3, 3, 300, 300, 0, True, 64),
     (2, 32, 8, 130, 400, 100, True, 0),    # B*H a multiple of 64: eight heads per XCD at a time
+    (2, 9, 3, 4096, 4608, 512, True, 0),   # 576 query tiles: more than the GPU holds at once
+    (1, 20, 20, 3333, 4000, 600, False, 0),  # 540 tiles, unmasked, ragged last tile
 ]
 
 

@@ -115,6 +115,26 @@ def test_bf16_shapes(B, H, n, causal, lens):
     np.testing.assert_allclose(lse[rows], rl[rows], rtol=0, atol=BF16_LSE_ATOL)
 
 
+@pytest.mark.parametrize("B,H,n,causal,lens", [
+    (4, 16, 2048, True, [2048, 1000, 300, 17]),   # 1024 query tiles, many of them padding
+    (2, 40, 1600, False, [1600, 999]),            # 1040 tiles, no mask, ragged lengths
+    (3, 24, 1100, True, None),                    # 648 tiles: a partial last round
+])
+def test_bf16_more_tiles_than_resident_workgroups(B, H, n, causal, lens):
+    """Shapes with more query tiles than the GPU holds workgroups at once (two per CU), with
+    padding tiles (wholly past a length) among the later ones, ragged lengths, no mask, and
+    a partial last wave of workgroups."""
+    q, k, v = workloads.prefill(B, H, n, 128, seed=3 * n + H, lens=lens, poison=lens is not None)
+    print(f"case: bf16 many tiles B={B} H={H} n={n} causal={causal} lens={lens}", flush=True)
+    o, lse = gpu_fwd(q, k, v, causal=causal, seq_lens=lens)
+    ro, rl = oracle.attention(q, k, v, causal=causal, seq_lens=lens)
+    rows = valid_rows(B, H, n, lens)
+    mx, mean = errs(o, ro, rows)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    check_padding(o, lse, lens)
+    np.testing.assert_allclose(lse[rows], rl[rows], rtol=0, atol=BF16_LSE_ATOL)
+
+
 def test_bf16_causal_prefill_workload():
     w = workloads.causal_prefill()
     print("case: causal prefill bf16 [4,32,2048,128]", flush=True)
