@@ -69,6 +69,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import subprocess
 import sys
@@ -990,7 +991,8 @@ def summarize_trace(trace_csv, line_file):
             kind = "decode_merge"
         else:
             kind = "other"
-        names.setdefault(kind, set()).add(name.split("(")[0][:80])
+        short = re.search(r"\w+_kernel(<[^>]*>)?", name)
+        names.setdefault(kind, set()).add(short.group(0) if short else name[:80])
         by_kind.setdefault(kind, []).append(dur)
     K = int(line["steps"])
     ti = line["trace_index"]
