@@ -35,6 +35,7 @@ constexpr float kSlack = 8.0f;        // log2 headroom of the accumulation refer
 
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) uint4 lds_uint4;
+typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ float other_half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -100,8 +101,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 
   const size_t n_pad = (size_t)n_blocks * kBN;
   const rsrc_t rq = make_rsrc(Q8 + (size_t)bh * n * kD, (uint32_t)L * kD);
-  const rsrc_t rk = make_rsrc(K8 + (size_t)bhk * n * kD, (uint32_t)L * kD);
-  const rsrc_t rv = make_rsrc(VT8 + (size_t)bhk * kD * n_pad, (uint32_t)(kD * n_pad));
 
   // Q^T operand: lane (query lq, half hl) holds dims 64 ks + 32 hl .. +31 for ks = 0, 1
   intx8 qop[2];
@@ -134,15 +133,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     const int D = 2 * ln + (p >> 2);
     v_src[i] = D * (int)n_pad + 16 * ((p & 3) ^ (ln & 3));
   }
-  auto issue_k = [&](int t, int buf) {
+  // Each tile is read through a descriptor whose base is the tile's first key (K: row
+  // t * 64; V^T: column t * 64), with the range ending at row L (K) or at the matrix end
+  // (V^T, whose padding columns are zeros), and each wave's 2 KiB slice of a tile sits at a
+  // scalar LDS offset: a fill costs no vector instruction.
+  const uint8_t* k_head = K8 + (size_t)bhk * n * kD;
+  const uint8_t* v_head = VT8 + (size_t)bhk * kD * n_pad;
+  const int lds_w = __builtin_amdgcn_readfirstlane(w * 2 * 1024);
+  auto issue_k = [&](int t, int buf) __attribute__((always_inline)) {
+    const int first = t * kBN;
+    const rsrc_t r = make_rsrc(k_head + (size_t)first * kD, (uint32_t)max(L - first, 0) * kD);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      load_lds16(rk, (lds_void*)&Ks[buf][(2 * w + i) * 1024], t * kBN * kD + k_src[i]);
+      load_lds16(r, (lds_void*)((lds_char*)(lds_void*)Ks[buf] + lds_w + i * 1024), k_src[i]);
   };
-  auto issue_v = [&](int t, int buf) {
+  auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
+    const int first = t * kBN;
+    const rsrc_t r = make_rsrc(v_head + first, (uint32_t)(kD * n_pad - first));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      load_lds16(rv, (lds_void*)&Vs[buf][(2 * w + i) * 1024], t * kBN + v_src[i]);
+      load_lds16(r, (lds_void*)((lds_char*)(lds_void*)Vs[buf] + lds_w + i * 1024), v_src[i]);
   };
 
   floatx16 acc[4];  // O^T: lane holds d = 32 db + 8 (r/4) + 4 hl + r%4 of query qi
@@ -162,7 +172,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   struct Tile {
     floatx16 s[2];  // raw scores: s[kb][r] is key k0 + 32 kb + 16 hl + r (masked: -inf)
   };
-  auto compute_s = [&](Tile& T, const uint8_t* Kt) {  // S^T = K Q^T, 4 MFMA
+  auto compute_s = [&](Tile& T, const uint8_t* Kt) __attribute__((always_inline)) {  // S^T = K Q^T, 4 MFMA
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) T.s[kb] = zero16;
 #pragma unroll
@@ -174,11 +184,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         T.s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qop[ks], T.s[kb], 0, 0, 0, 0, 0, 0);
       }
   };
-  auto need_mask = [&](int t) {
+  auto need_mask = [&](int t) __attribute__((always_inline)) {
     const int k0 = t * kBN;
     return (k0 + kBN > L) || (causal && k0 + kBN - 1 > wave_q_first);
   };
-  auto apply_mask = [&](Tile& T, int k0) {
+  auto apply_mask = [&](Tile& T, int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
       }
   };
   // tile maximum in log2 units; c > 0, so max(raw) * c is the max of the rounded products
-  auto row_max = [&](const Tile& T, float c) {
+  auto row_max = [&](const Tile& T, float c) __attribute__((always_inline)) {
     float mx = __builtin_fmaxf(T.s[0][0], T.s[0][1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, T.s[0][r]), T.s[0][r + 1]);
@@ -196,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, T.s[1][r]), T.s[1][r + 1]);
     return other_half_max(mx) * c;
   };
-  auto weights = [&](const Tile& T, float c, float m_use, intx8& pop) {  // byte e = 16 kb + r
+  auto weights = [&](const Tile& T, float c, float m_use, intx8& pop) __attribute__((always_inline)) {  // byte e = 16 kb + r
 #pragma unroll
     for (int wd = 0; wd < 8; ++wd) {
       const int kb = wd >> 2, r0 = 4 * (wd & 3);
@@ -208,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
       pop[wd] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
     }
   };
-  auto raise_ref = [&]() {
+  auto raise_ref = [&]() __attribute__((always_inline)) {
     if (__any(m_cur > m_ref + kSlack)) {
       const float m_new = __builtin_fmaxf(__builtin_fmaxf(m_ref, m_cur), -1e30f);
       const float alpha = __builtin_amdgcn_exp2f(__builtin_fmaxf(m_ref, -1e30f) - m_new);  // 0 from empty
@@ -224,53 +234,70 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   // One pipelined step: the weights of tile t (in `cur`) are formed while the matrix cores
   // compute the scores of tile t+1 (into `nxt`); then P(t) V(t) runs while the maximum of
   // tile t+1 is taken and the previous products enter acc.  K loads run two tiles ahead,
-  // V loads one.
+  // V loads one.  Every wave runs these steps up to the workgroup's last tile, so the step
+  // is straight-line code; a wave whose diagonal lies before the last tile scores that tile
+  // needlessly (its maximum then moves m_cur past any use: the last step skips the wave).
   // Block scales of K (tiles t and t+1) and V (tile t), read one step ahead: a scalar load
   // inside the step would make the wave wait for every LDS read in flight as well.
   float ks_cur = 0.f, ks_nxt = 0.f, vs_cur = 0.f;
-  auto step = [&](int t, Tile& cur, Tile& nxt) {
-    if (t + 2 < n_tiles) issue_k(t + 2, t & 1);
-    if (t + 1 < n_tiles) issue_v(t + 1, (t + 1) & 1);
-    if (t < wave_tiles) {
-      const bool do_next = t + 1 < wave_tiles;
-      raise_ref();
-      const float m_use = __builtin_fmaxf(m_cur, -1e30f);
-      const float f = __builtin_amdgcn_exp2f(m_use - __builtin_fmaxf(m_ref, -1e30f));
-      intx8 pop;
-      if (do_next) compute_s(nxt, Ks[(t + 1) & 1]);
-      weights(cur, c_q * ks_cur, m_use, pop);
-      // P.V in two halves of 64 dimensions (keeps 32 product registers live), the row sum
-      // of the rounded weights, and the next tile's mask and maximum in between
-      const float fv = f * vs_cur;
-      floatx16 lsum;
+  const int t_last = n_tiles - 1;
+  auto pv_update = [&](const intx8& pop, const uint8_t* Vt, float fv, auto&& between)
+      __attribute__((always_inline)) {
+    // P.V in two halves of 64 dimensions (keeps 32 product registers live), the row sum of
+    // the rounded weights, and `between` (the next tile's mask and maximum) in between
+    floatx16 lsum;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        floatx16 tmp[2];
+    for (int half = 0; half < 2; ++half) {
+      floatx16 tmp[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int D = 64 * half + 32 * i + lq;
-          const intx8 a = read32(Vs[t & 1], v_off(D, hl), v_off(D, 2 + hl));
-          tmp[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pop, zero16, 0, 0, 0, 0, 0, 0);
-        }
-        if (half == 0) {
-          lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pop, zero16, 0, 0, 0, 0, 0, 0);
-          if (do_next) {
-            if (need_mask(t + 1)) apply_mask(nxt, (t + 1) * kBN);
-            m_cur = __builtin_fmaxf(m_cur, row_max(nxt, c_q * ks_nxt));
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[2 * half + i][r] = fmaf(tmp[i][r], fv, acc[2 * half + i][r]);
+      for (int i = 0; i < 2; ++i) {
+        const int D = 64 * half + 32 * i + lq;
+        const intx8 a = read32(Vt, v_off(D, hl), v_off(D, 2 + hl));
+        tmp[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pop, zero16, 0, 0, 0, 0, 0, 0);
       }
-      l_acc = fmaf(lsum[0], f, l_acc);
+      if (half == 0) {
+        lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pop, zero16, 0, 0, 0, 0, 0, 0);
+        between();
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[2 * half + i][r] = fmaf(tmp[i][r], fv, acc[2 * half + i][r]);
     }
+    return lsum[0];
+  };
+  auto step = [&](int t, Tile& cur, Tile& nxt) __attribute__((always_inline)) {
+    if (t + 2 < n_tiles) issue_k(t + 2, t & 1);
+    issue_v(t + 1, (t + 1) & 1);
+    raise_ref();
+    const float m_use = __builtin_fmaxf(m_cur, -1e30f);
+    const float f = __builtin_amdgcn_exp2f(m_use - __builtin_fmaxf(m_ref, -1e30f));
+    intx8 pop;
+    compute_s(nxt, Ks[(t + 1) & 1]);
+    weights(cur, c_q * ks_cur, m_use, pop);
+    const float lsum = pv_update(pop, Vs[t & 1], f * vs_cur, [&]() __attribute__((always_inline)) {
+      // tile t+1 is used unless it is the last tile and lies past this wave's diagonal
+      if ((t + 1 < wave_tiles || t + 1 < t_last) && need_mask(t + 1)) apply_mask(nxt, (t + 1) * kBN);
+      m_cur = __builtin_fmaxf(m_cur, row_max(nxt, c_q * ks_nxt));
+    });
+    l_acc = fmaf(lsum, f, l_acc);
     ks_cur = ks_nxt;
     ks_nxt = ks_row[min(t + 2, n_blocks - 1)];
     vs_cur = vs_row[min(t + 1, n_blocks - 1)];
     __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the next tiles (and scales) landed
     __syncthreads();
+  };
+  // the last tile: the rest of its work, no loads, no barrier
+  auto step_last = [&](int t, Tile& cur) __attribute__((always_inline)) {
+    if (t < wave_tiles) {
+      raise_ref();
+      const float m_use = __builtin_fmaxf(m_cur, -1e30f);
+      const float f = __builtin_amdgcn_exp2f(m_use - __builtin_fmaxf(m_ref, -1e30f));
+      intx8 pop;
+      weights(cur, c_q * ks_cur, m_use, pop);
+      const float lsum = pv_update(pop, Vs[t & 1], f * vs_cur, []() {});
+      l_acc = fmaf(lsum, f, l_acc);
+    }
   };
 
   // ---- prologue: K(0), V(0), K(1) in flight; scores and maximum of tile 0
@@ -288,10 +315,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   vs_cur = vs_row[0];
   __syncthreads();  // every wave is done with K(0) before K(2) overwrites its buffer
 
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = 0; t < t_last; t += 2) {
     step(t, ta, tb);
-    if (t + 1 < n_tiles) step(t + 1, tb, ta);
+    if (t + 1 < t_last) step(t + 1, tb, ta);
   }
+  if ((t_last & 1) == 0)
+    step_last(t_last, ta);
+  else
+    step_last(t_last, tb);
 
   // ---- epilogue: o = u / l (l is the whole row's sum: every lane of the MFMA column has it)
   if (qi < n) {
