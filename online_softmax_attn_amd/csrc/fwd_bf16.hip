@@ -97,8 +97,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // Q, O, LSE hold n query rows; K, V hold n_kv key rows.  Query row r sits at position
   // q_start + r of the key sequence (the causal mask and the window count positions); the
   // plain call has n_kv = n and q_start = 0.  Lengths (lens) apply to plain calls only.
-  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][kTileElems];
-  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][kTileElems];
+  // K tiles in slots 0 and 1, V tiles in slots 2 and 3 (one LDS object: the compiler then
+  // keeps the non-aliasing of the four slots declared below)
+  __shared__ __attribute__((aligned(1024))) bf16 tiles[4][kTileElems];
 
   const int HB = H * B;
   int qt, bh;
@@ -177,15 +178,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   auto lds_dst = [&](bf16* tile, int i) __attribute__((always_inline)) {
     return (lds_void*)((lds_char*)(lds_void*)tile + lds_w + i * 1024);
   };
-  auto issue_k = [&](int t, int buf) __attribute__((always_inline)) {
+  auto issue_k = [&](int t, bf16* Kd) __attribute__((always_inline)) {
     const rsrc_t r = tile_rsrc(k_head, t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_lds16(r, lds_dst(Ks[buf], i), k_src[i]);
+    for (int i = 0; i < 4; ++i) load_lds16(r, lds_dst(Kd, i), k_src[i]);
   };
-  auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
+  auto issue_v = [&](int t, bf16* Vd) __attribute__((always_inline)) {
     const rsrc_t r = tile_rsrc(v_head, t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_lds16(r, lds_dst(Vs[buf], i), v_src[i]);
+    for (int i = 0; i < 4; ++i) load_lds16(r, lds_dst(Vd, i), v_src[i]);
   };
 
   floatx16 acc[4];  // O^T, d blocks of 32: lane holds d = 32*db + 8*(r/4) + 4*hl + r%4
@@ -338,16 +339,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // One pipelined step: the weights of tile t (in `cur`) are formed while the matrix cores
   // compute the scores of tile t+1 (into `nxt`); then P(t) V(t) is accumulated.  Loads run
-  // two tiles ahead for K, one for V.  Every wave of the workgroup runs these steps up to
-  // the workgroup's last tile, so the step is one straight block and the weights' FMAs and
-  // exps interleave with the score products; a wave whose diagonal lies before the last
-  // tile scores that tile needlessly but never uses it (step_last skips it).
+  // two tiles ahead for K (into Kf), one for V (into Vf); the step reads K(t+1) from Kr and
+  // V(t) from Vr.  Every wave of the workgroup runs these steps up to the workgroup's last
+  // tile, so the step is one straight block and the weights' FMAs and exps interleave with
+  // the score products; a wave whose diagonal lies before the last tile scores that tile
+  // needlessly but never uses it (step_last skips it).
   const int t_last = n_tiles - 1;
-  auto step = [&](int t, Tile& cur, Tile& nxt) __attribute__((always_inline)) {
-    if (t + 2 < n_tiles) issue_k(t + 2, t & 1);
-    issue_v(t + 1, (t + 1) & 1);
+  auto step = [&](int t, Tile& cur, Tile& nxt, bf16* Kf, bf16* Vf, const bf16* Kr,
+                  const bf16* Vr) __attribute__((always_inline)) {
+    if (t + 2 < n_tiles) issue_k(t + 2, Kf);
+    issue_v(t + 1, Vf);
     bf16x8 pop[4];
-    compute_s(nxt, Ks[(t + 1) & 1]);
+    compute_s(nxt, Kr);
     const float psum = weights(cur, pop);
     __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
 #pragma unroll
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
     }
     checked_weights(cur, pop, psum);
-    pv(Vs[t & 1], pop);
+    pv(Vr, pop);
     __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 8, 1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -371,36 +374,49 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
   // The last tile: its weights and P V, no loads, no barrier after it (its K tile was read in
   // the step before, whose barrier frees the K buffers for the epilogue).
-  auto step_last = [&](int t, Tile& cur) __attribute__((always_inline)) {
+  auto step_last = [&](int t, Tile& cur, const bf16* Vr) __attribute__((always_inline)) {
     if (t < wave_tiles) {
       bf16x8 pop[4];
       checked_weights(cur, pop, weights(cur, pop));
-      pv(Vs[t & 1], pop);
+      pv(Vr, pop);
     }
   };
 
-  // ---- prologue: K(t0), V(t0), K(t0+1) in flight; scores and max of tile t0.  Tile t
-  // always lives in buffer t & 1, its scores in ta when t - t0 is even, else in tb.
+  // The sweep runs inside one function whose four tile buffers are declared non-aliasing:
+  // the compiler then knows that the fills a step issues do not touch the tiles it reads,
+  // and leaves the wait for them to the step's closing waitcnt (it would otherwise wait for
+  // the fills just issued before the first LDS read after them).  Tile t lives in buffer
+  // (t - t0) & 1; its scores in ta when t - t0 is even, else in tb.
   const int t0 = t_first;
-  issue_k(t0, t0 & 1);
-  issue_v(t0, t0 & 1);
-  if (t0 + 1 < n_tiles) issue_k(t0 + 1, (t0 + 1) & 1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  Tile ta, tb;
-  compute_s(ta, Ks[t0 & 1]);
-  if (need_mask(t0)) apply_mask(ta, t0 * kBN);
-  raise_ref(row_max(ta));
-  __syncthreads();  // every wave is done with K(t0) before K(t0+2) overwrites its buffer
+  auto sweep = [&](bf16* __restrict__ k0, bf16* __restrict__ k1, bf16* __restrict__ v0,
+                   bf16* __restrict__ v1) {
+    // ---- prologue: K(t0), V(t0), K(t0+1) in flight; scores and max of tile t0
+    issue_k(t0, k0);
+    issue_v(t0, v0);
+    if (t0 + 1 < n_tiles) issue_k(t0 + 1, k1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    Tile ta, tb;
+    compute_s(ta, k0);
+    if (need_mask(t0)) apply_mask(ta, t0 * kBN);
+    raise_ref(row_max(ta));
+    __syncthreads();  // every wave is done with K(t0) before K(t0+2) overwrites its buffer
 
-  for (int t = t0; t < t_last; t += 2) {
-    step(t, ta, tb);
-    if (t + 1 < t_last) step(t + 1, tb, ta);
-  }
-  if (((t_last - t0) & 1) == 0)
-    step_last(t_last, ta);
-  else
-    step_last(t_last, tb);
+    for (int t = t0; t < t_last; t += 2) {
+      step(t, ta, tb, k0, v1, k1, v0);
+      if (t + 1 < t_last) step(t + 1, tb, ta, k1, v0, k0, v1);
+    }
+    if (((t_last - t0) & 1) == 0)
+      step_last(t_last, ta, v0);
+    else
+      step_last(t_last, tb, v1);
+  };
+  // The buffers are passed at an offset the optimiser cannot see (zero at run time): with
+  // constant arguments it would substitute the constants into the body before inlining it,
+  // and the non-aliasing of the parameters would be lost.
+  int hidden_zero;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(hidden_zero));
+  sweep(tiles[0] + hidden_zero, tiles[1] + hidden_zero, tiles[2] + hidden_zero, tiles[3] + hidden_zero);
 
   // ---- epilogue: o = u / l, staged through LDS so that each store instruction writes four
   // whole 256-byte rows of O.  Every wave has passed the last step's barrier, so the K
@@ -409,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const float l_tot = other_half_sum(l_run);
   const bool valid = qi < L;
   const float inv = 1.0f / l_tot;
-  bf16* stage = &Ks[0][0] + w * (32 * kD);
+  bf16* stage = &tiles[0][0] + w * (32 * kD);
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
