@@ -68,8 +68,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     const float* __restrict__ v_scale, bf16* __restrict__ O, float* __restrict__ LSE,
     const int32_t* __restrict__ lens, int B, int H, int Hkv, int n, int n_qtiles, int n_blocks,
     int causal, float scale) {
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks[2][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs[2][kTileBytes];
+  // K tiles in slots 0 and 1, V^T tiles in slots 2 and 3 (one LDS object: the compiler then
+  // keeps the non-aliasing of the four slots declared below)
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[4][kTileBytes];
 
   const int HB = H * B;
   const GridSlot slot = causal_grid_slot((int)blockIdx.x, HB, n_qtiles);  // heaviest first
@@ -140,19 +141,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const uint8_t* k_head = K8 + (size_t)bhk * n * kD;
   const uint8_t* v_head = VT8 + (size_t)bhk * kD * n_pad;
   const int lds_w = __builtin_amdgcn_readfirstlane(w * 2 * 1024);
-  auto issue_k = [&](int t, int buf) __attribute__((always_inline)) {
+  auto issue_k = [&](int t, uint8_t* Kd) __attribute__((always_inline)) {
     const int first = t * kBN;
     const rsrc_t r = make_rsrc(k_head + (size_t)first * kD, (uint32_t)max(L - first, 0) * kD);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      load_lds16(r, (lds_void*)((lds_char*)(lds_void*)Ks[buf] + lds_w + i * 1024), k_src[i]);
+      load_lds16(r, (lds_void*)((lds_char*)(lds_void*)Kd + lds_w + i * 1024), k_src[i]);
   };
-  auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
+  auto issue_v = [&](int t, uint8_t* Vd) __attribute__((always_inline)) {
     const int first = t * kBN;
     const rsrc_t r = make_rsrc(v_head + first, (uint32_t)(kD * n_pad - first));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      load_lds16(r, (lds_void*)((lds_char*)(lds_void*)Vs[buf] + lds_w + i * 1024), v_src[i]);
+      load_lds16(r, (lds_void*)((lds_char*)(lds_void*)Vd + lds_w + i * 1024), v_src[i]);
   };
 
   floatx16 acc[4];  // O^T: lane holds d = 32 db + 8 (r/4) + 4 hl + r%4 of query qi
@@ -266,16 +267,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     }
     return lsum[0];
   };
-  auto step = [&](int t, Tile& cur, Tile& nxt) __attribute__((always_inline)) {
-    if (t + 2 < n_tiles) issue_k(t + 2, t & 1);
-    issue_v(t + 1, (t + 1) & 1);
+  auto step = [&](int t, Tile& cur, Tile& nxt, uint8_t* Kf, uint8_t* Vf, const uint8_t* Kr,
+                  const uint8_t* Vr) __attribute__((always_inline)) {
+    if (t + 2 < n_tiles) issue_k(t + 2, Kf);
+    issue_v(t + 1, Vf);
     raise_ref();
     const float m_use = __builtin_fmaxf(m_cur, -1e30f);
     const float f = __builtin_amdgcn_exp2f(m_use - __builtin_fmaxf(m_ref, -1e30f));
     intx8 pop;
-    compute_s(nxt, Ks[(t + 1) & 1]);
+    compute_s(nxt, Kr);
     weights(cur, c_q * ks_cur, m_use, pop);
-    const float lsum = pv_update(pop, Vs[t & 1], f * vs_cur, [&]() __attribute__((always_inline)) {
+    const float lsum = pv_update(pop, Vr, f * vs_cur, [&]() __attribute__((always_inline)) {
       // tile t+1 is used unless it is the last tile and lies past this wave's diagonal
       if ((t + 1 < wave_tiles || t + 1 < t_last) && need_mask(t + 1)) apply_mask(nxt, (t + 1) * kBN);
       m_cur = __builtin_fmaxf(m_cur, row_max(nxt, c_q * ks_nxt));
@@ -288,41 +290,54 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     __syncthreads();
   };
   // the last tile: the rest of its work, no loads, no barrier
-  auto step_last = [&](int t, Tile& cur) __attribute__((always_inline)) {
+  auto step_last = [&](int t, Tile& cur, const uint8_t* Vr) __attribute__((always_inline)) {
     if (t < wave_tiles) {
       raise_ref();
       const float m_use = __builtin_fmaxf(m_cur, -1e30f);
       const float f = __builtin_amdgcn_exp2f(m_use - __builtin_fmaxf(m_ref, -1e30f));
       intx8 pop;
       weights(cur, c_q * ks_cur, m_use, pop);
-      const float lsum = pv_update(pop, Vs[t & 1], f * vs_cur, []() {});
+      const float lsum = pv_update(pop, Vr, f * vs_cur, []() {});
       l_acc = fmaf(lsum, f, l_acc);
     }
   };
 
-  // ---- prologue: K(0), V(0), K(1) in flight; scores and maximum of tile 0
-  issue_k(0, 0);
-  issue_v(0, 0);
-  if (n_tiles > 1) issue_k(1, 1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  Tile ta, tb;
-  compute_s(ta, Ks[0]);
-  if (need_mask(0)) apply_mask(ta, 0);
-  m_cur = row_max(ta, c_q * ks_row[0]);
-  ks_cur = ks_row[0];
-  ks_nxt = ks_row[min(1, n_blocks - 1)];
-  vs_cur = vs_row[0];
-  __syncthreads();  // every wave is done with K(0) before K(2) overwrites its buffer
+  // The sweep runs inside one function whose four tile slots are declared non-aliasing: the
+  // compiler then knows that the fills a step issues do not touch the tiles it reads, and
+  // leaves the wait for them to the step's closing waitcnt (it would otherwise wait for the
+  // fills just issued before the first LDS read after them).  Tile t lives in slot t & 1.
+  auto sweep = [&](uint8_t* __restrict__ k0, uint8_t* __restrict__ k1, uint8_t* __restrict__ v0,
+                   uint8_t* __restrict__ v1) {
+    // ---- prologue: K(0), V(0), K(1) in flight; scores and maximum of tile 0
+    issue_k(0, k0);
+    issue_v(0, v0);
+    if (n_tiles > 1) issue_k(1, k1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    Tile ta, tb;
+    compute_s(ta, k0);
+    if (need_mask(0)) apply_mask(ta, 0);
+    m_cur = row_max(ta, c_q * ks_row[0]);
+    ks_cur = ks_row[0];
+    ks_nxt = ks_row[min(1, n_blocks - 1)];
+    vs_cur = vs_row[0];
+    __syncthreads();  // every wave is done with K(0) before K(2) overwrites its buffer
 
-  for (int t = 0; t < t_last; t += 2) {
-    step(t, ta, tb);
-    if (t + 1 < t_last) step(t + 1, tb, ta);
-  }
-  if ((t_last & 1) == 0)
-    step_last(t_last, ta);
-  else
-    step_last(t_last, tb);
+    for (int t = 0; t < t_last; t += 2) {
+      step(t, ta, tb, k0, v1, k1, v0);
+      if (t + 1 < t_last) step(t + 1, tb, ta, k1, v0, k0, v1);
+    }
+    if ((t_last & 1) == 0)
+      step_last(t_last, ta, v0);
+    else
+      step_last(t_last, tb, v1);
+  };
+  // The slots are passed at an offset the optimiser cannot see (zero at run time): with
+  // constant arguments it would substitute the constants into the body before inlining it,
+  // and the non-aliasing of the parameters would be lost.
+  int hidden_zero;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(hidden_zero));
+  sweep(tiles[0] + hidden_zero, tiles[1] + hidden_zero, tiles[2] + hidden_zero, tiles[3] + hidden_zero);
 
   // ---- epilogue: o = u / l (l is the whole row's sum: every lane of the MFMA column has it)
   if (qi < n) {
