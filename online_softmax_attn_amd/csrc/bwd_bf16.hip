@@ -85,8 +85,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     float* __restrict__ Dv, const int32_t* __restrict__ lens, float* __restrict__ dQ, int B,
     int H, int Hkv, int n,
     int n_qtiles, int causal, int window, float c_log2, float scale) {
-  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][kTileElems];
-  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][kTileElems];
+  // K tiles in slots 0 and 1, V tiles in slots 2 and 3 (one LDS object: the compiler then
+  // keeps the non-aliasing of the four slots declared below)
+  __shared__ __attribute__((aligned(1024))) bf16 tiles[4][kTileElems];
   constexpr int kBM = 128;
 
   const int HB = H * B;
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   }
 
   const int kend = causal ? min(L, m0 + kBM) : L;
-  const int n_tiles = (kend + kTile - 1) / kTile;  // tiles [t_first, n_tiles); tile t in buffer t & 1
+  const int n_tiles = (kend + kTile - 1) / kTile;  // tiles [t_first, n_tiles)
   const int t_first = window ? max(0, m0 - window + 1) / kTile : 0;
   const int wave_q_first = m0 + 32 * w, wave_q_last = wave_q_first + 31;
   const int wave_tiles = causal ? min(n_tiles, wave_q_last / kTile + 1) : n_tiles;
@@ -159,20 +160,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  fill.issue(rk, Ks[t_first & 1], t_first, w);
-  fill.issue(rv, Vs[t_first & 1], t_first, w);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int t = t_first; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  // One step: tile t+1 is fetched into (Kf, Vf) while tile t is used from (Kt, Vt).
+  auto step = [&](int t, bf16* Kf, bf16* Vf, const bf16* Kt, const bf16* Vt)
+      __attribute__((always_inline)) {
     if (t + 1 < n_tiles) {
-      fill.issue(rk, Ks[buf ^ 1], t + 1, w);
-      fill.issue(rv, Vs[buf ^ 1], t + 1, w);
+      fill.issue(rk, Kf, t + 1, w);
+      fill.issue(rv, Vf, t + 1, w);
     }
     if (t < wave_tiles) {
-      const bf16* Kt = Ks[buf];
-      const bf16* Vt = Vs[buf];
       const int k0 = t * kTile;
       floatx16 s[2], dp[2];  // S^T and dP^T: lane holds key 32 kb + 8 (r/4) + 4 hl + r%4
 #pragma unroll
@@ -233,9 +228,30 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         for (int db = 0; db < 4; ++db)
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Kt, grp, db, lane), dsop[grp], acc[db], 0, 0, 0);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of tile t+1 has landed
+    __syncthreads();
+  };
+  // The sweep runs inside one function whose four tile slots are declared non-aliasing: the
+  // compiler then knows that a step's fills do not touch the tile it reads, and leaves the
+  // wait for them to the step's closing waitcnt (it would otherwise wait for the fills just
+  // issued before the first LDS read).  Tile t lives in slot (t - t_first) & 1.
+  auto sweep = [&](bf16* __restrict__ k0, bf16* __restrict__ k1, bf16* __restrict__ v0,
+                   bf16* __restrict__ v1) {
+    fill.issue(rk, k0, t_first, w);
+    fill.issue(rv, v0, t_first, w);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+    for (int t = t_first; t < n_tiles; t += 2) {
+      step(t, k1, v1, k0, v0);
+      if (t + 1 < n_tiles) step(t + 1, k0, v0, k1, v1);
+    }
+  };
+  // The slots are passed at an offset the optimiser cannot see (zero at run time): with
+  // constant arguments it would substitute the constants into the body before inlining it,
+  // and the non-aliasing of the parameters would be lost.
+  int hidden_zero;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(hidden_zero));
+  sweep(tiles[0] + hidden_zero, tiles[1] + hidden_zero, tiles[2] + hidden_zero, tiles[3] + hidden_zero);
 
   if (qi < n) {
     // the lane's half index is taken afresh from the lane id (mbcnt) rather than kept live
@@ -267,13 +283,21 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     const int32_t* __restrict__ lens, float* __restrict__ dK, float* __restrict__ dV, int B,
-    int H, int Hkv, int n, int causal, int window, float c_log2, float scale) {
-  __shared__ __attribute__((aligned(1024))) bf16 Qs[2][kTileElems];
-  __shared__ __attribute__((aligned(1024))) bf16 Gs[2][kTileElems];
-  __shared__ __attribute__((aligned(16))) float Ls[2][kTile];  // log2-unit LSE; +inf on padding
-  __shared__ __attribute__((aligned(16))) float Ds[2][kTile];
-  // weights handed from V-wave to K-wave: [pair][block][register group][lane], four fp32 each
-  __shared__ __attribute__((aligned(16))) floatx4 Ps[4][2][4][64];
+    int H, int Hkv, int n, int causal, int window, float c_log2, float scale, float log2e) {
+  // one LDS object (the compiler then keeps the non-aliasing of the K-waves' slots below)
+  struct Tiles {
+    bf16 q[2][kTileElems];
+    bf16 g[2][kTileElems];     // dO
+    float l[2][kTile];         // log2-unit LSE; +inf on padding
+    float d[2][kTile];
+    floatx4 p[4][2][4][64];    // weights handed from V-wave to K-wave: [pair][block][group][lane]
+  };
+  __shared__ __attribute__((aligned(1024))) Tiles lds;
+  auto& Qs = lds.q;
+  auto& Gs = lds.g;
+  auto& Ls = lds.l;
+  auto& Ds = lds.d;
+  auto& Ps = lds.p;
   constexpr int kBK = 128;
 
   const int HB = Hkv * B;
@@ -334,23 +358,25 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
     const int c = pc ^ (((r & 3) << 2) | ((r >> 2) & 3));
     src[i] = (r * kD + 8 * c) * 2;
   }
-  auto issue = [&](int it, int buf) {  // K-waves only
+  auto issue = [&](int it, bf16* Qd, bf16* Gd) __attribute__((always_inline)) {  // K-waves only
     const int bh = bh0 + it / nt, t = t0 + it % nt;
     const size_t base = (size_t)bh * n * kD;
     const rsrc_t rq = make_rsrc(Q + base, valid_bytes);
     const rsrc_t rg = make_rsrc(dO + base, valid_bytes);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      load_lds16(rq, (lds_void*)&Qs[buf][(4 * kw + i) * 512], t * kTile * kD * 2 + src[i]);
-      load_lds16(rg, (lds_void*)&Gs[buf][(4 * kw + i) * 512], t * kTile * kD * 2 + src[i]);
+      load_lds16(rq, (lds_void*)&Qd[(4 * kw + i) * 512], t * kTile * kD * 2 + src[i]);
+      load_lds16(rg, (lds_void*)&Gd[(4 * kw + i) * 512], t * kTile * kD * 2 + src[i]);
     }
   };
-  // the tile's LSE (log2 units, +inf on padding) and D, one query per lane of wave 0: loaded
-  // into registers when the tile's loads are issued and written to LDS at the end of the
-  // step, so the wave never waits on them mid-step
+  // the tile's LSE (+inf on padding) and D, one query per lane of wave 0: loaded into
+  // registers when the tile's loads are issued and written to LDS (the LSE in log2 units)
+  // at the end of the step, so the wave never waits on them mid-step.  log2e arrives as an
+  // argument: a literal factor would be folded into the load's branch, and the wave would
+  // wait for the load there.
   auto load_ld = [&](int it, float& l, float& d) {
     const int bh = bh0 + it / nt, q = (t0 + it % nt) * kTile + tid;
-    l = q < L ? LSE[(size_t)bh * n + q] * ATTN_LOG2E : INFINITY;
+    l = q < L ? LSE[(size_t)bh * n + q] : INFINITY;
     d = q < L ? Dv[(size_t)bh * n + q] : 0.f;
   };
   auto skip = [&](int t, int qb) {
@@ -370,11 +396,11 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  if (!vwave) issue(0, 0);
+  if (!vwave) issue(0, Qs[0], Gs[0]);
   if (tid < kTile) {
     float l, d;
     load_ld(0, l, d);
-    Ls[0][tid] = l;
+    Ls[0][tid] = l * log2e;
     Ds[0][tid] = d;
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -440,19 +466,19 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Gt, 2 * qb + g, db, lane), pop[qb][g], acc[db], 0, 0, 0);
       }
       if (it + 1 < steps && tid < kTile) {  // the previous step's readers are past its barrier
-        Ls[buf ^ 1][tid] = l_next;
+        Ls[buf ^ 1][tid] = l_next * log2e;
         Ds[buf ^ 1][tid] = d_next;
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   } else {
-    for (int it = 0; it < steps; ++it) {
-      const int buf = it & 1;
-      if (it + 1 < steps) issue(it + 1, buf ^ 1);
+    // One K-wave step: tile it+1 is fetched into (Qf, Gf) while tile it is used from (Qt, Gt)
+    // with its D values (Dt) and the V-waves' weights (P).
+    auto kstep = [&](int it, bf16* Qf, bf16* Gf, const bf16* Qt, const bf16* Gt,
+                     const float* Dt, const floatx4* P) __attribute__((always_inline)) {
+      if (it + 1 < steps) issue(it + 1, Qf, Gf);
       const int t = t0 + it % nt;
-      const bf16* Qt = Qs[buf];
-      const bf16* Gt = Gs[buf];
       floatx16 dp[2];  // dP: lane holds query q0 + 8 (r/4) + 4 hl + r%4 of key kj
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -470,7 +496,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Ds[buf][32 * qb + 8 * a + 4 * hl]);
+          const floatx4 d4 = *reinterpret_cast<const floatx4*>(&Dt[32 * qb + 8 * a + 4 * hl]);
 #pragma unroll
           for (int c = 0; c < 4; ++c) dp[qb][4 * a + c] -= d4[c];
         }
@@ -481,7 +507,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
         bf16x8 dsop[2];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const floatx4 p4 = Ps[pair][qb][a][lane];
+          const floatx4 p4 = P[((2 * pair + qb) * 4 + a) * 64 + lane];
           floatx4 ds4;
 #pragma unroll
           for (int c = 0; c < 4; ++c) ds4[c] = p4[c] * dp[qb][4 * a + c];  // dS = P (dP - D)
@@ -495,9 +521,28 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
           for (int db = 0; db < 4; ++db)  // dK^T += Q^T dS
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Qt, 2 * qb + g, db, lane), dsop[g], acc[db], 0, 0, 0);
       }
-      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's share of tile it+1 has landed
       __syncthreads();
-    }
+    };
+    // The K-waves' sweep runs inside one function whose LDS slots are declared
+    // non-aliasing: the compiler then knows that a step's fills do not touch what it reads,
+    // and leaves the wait for them to the step's closing waitcnt (it would otherwise wait
+    // for the fills just issued before the first LDS read).  Tile it lives in slot it & 1.
+    auto ksweep = [&](bf16* __restrict__ q0, bf16* __restrict__ q1, bf16* __restrict__ g0,
+                      bf16* __restrict__ g1, float* __restrict__ d0, float* __restrict__ d1,
+                      floatx4* __restrict__ p) {
+      for (int it = 0; it < steps; it += 2) {
+        kstep(it, q1, g1, q0, g0, d0, p);
+        if (it + 1 < steps) kstep(it + 1, q0, g0, q1, g1, d1, p);
+      }
+    };
+    // The slots are passed at an offset the optimiser cannot see (zero at run time): with
+    // constant arguments it would substitute the constants into the body before inlining
+    // it, and the non-aliasing of the parameters would be lost.
+    int hidden_zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(hidden_zero));
+    ksweep(Qs[0] + hidden_zero, Qs[1] + hidden_zero, Gs[0] + hidden_zero, Gs[1] + hidden_zero,
+           Ds[0] + hidden_zero, Ds[1] + hidden_zero, &Ps[0][0][0][0] + hidden_zero);
   }
 
   if (kj < n) {
@@ -537,6 +582,6 @@ hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf
   const int n_ktiles = (n + 127) / 128;
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)n_ktiles * batch * kv_heads), dim3(kPairThreads),
                      0, stream, q, k, v, dout, lse, Dv, seq_lens, dk, dv, batch, heads, kv_heads,
-                     n, causal, window, c_log2, scale);
+                     n, causal, window, c_log2, scale, ATTN_LOG2E);
   return hipGetLastError();
 }
