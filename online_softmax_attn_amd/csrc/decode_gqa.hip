@@ -62,10 +62,9 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, void* __restrict__ ws,
     int H, int Hkv, int num_blocks, int max_blocks_per_seq, int max_seq_len, int window,
     int max_splits, int split_blocks, float c_log2, size_t n_part) {
-  // one array per ring slot: the compiler then sees that a fill of one slot and the reads of
-  // another do not overlap and does not make the reads wait for the fill
-  __shared__ __attribute__((aligned(1024))) bf16 K0[kTileElems], K1[kTileElems], K2[kTileElems];
-  __shared__ __attribute__((aligned(1024))) bf16 V0[kTileElems], V1[kTileElems], V2[kTileElems];
+  // K ring slots 0-2, V ring slots 3-5 (one LDS object: the compiler then keeps the
+  // non-aliasing of the slots declared below)
+  __shared__ __attribute__((aligned(1024))) bf16 tiles[2 * kStages][kTileElems];
 
   const int G = H / Hkv;
   const int chunks = (G + kCols - 1) / kCols;
@@ -117,12 +116,17 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(
   const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);
 
   // one tile: tile t is in (Kt, Vt); tile t+2 is fetched into (Kf, Vf), the slot of t-1
-  lds_bf16* k0 = (lds_bf16*)K0;
-  lds_bf16* k1 = (lds_bf16*)K1;
-  lds_bf16* k2 = (lds_bf16*)K2;
-  lds_bf16* v0 = (lds_bf16*)V0;
-  lds_bf16* v1 = (lds_bf16*)V1;
-  lds_bf16* v2 = (lds_bf16*)V2;
+  // The slots are addressed at an offset the optimiser cannot see (zero at run time): with
+  // constant arguments it would substitute the constants into the ring function below
+  // before inlining it, and the non-aliasing of its parameters would be lost.
+  int hidden_zero;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(hidden_zero));
+  lds_bf16* k0 = (lds_bf16*)(tiles[0] + hidden_zero);
+  lds_bf16* k1 = (lds_bf16*)(tiles[1] + hidden_zero);
+  lds_bf16* k2 = (lds_bf16*)(tiles[2] + hidden_zero);
+  lds_bf16* v0 = (lds_bf16*)(tiles[3] + hidden_zero);
+  lds_bf16* v1 = (lds_bf16*)(tiles[4] + hidden_zero);
+  lds_bf16* v2 = (lds_bf16*)(tiles[5] + hidden_zero);
   // The whole ring runs inside one function whose slot pointers are declared non-aliasing:
   // the compiler then knows that a fill of one slot does not touch the slot being read and
   // leaves the wait for tile t to the explicit vmcnt below (it would otherwise drain every
@@ -175,16 +179,18 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s, 0, 0, 0);
       }
       // ---- mask (end of the split or sequence, window start), online update
-      const bool edge = (t0 + kTile > tok_end) || (t0 < kbeg);
-      float mx = -INFINITY;
+      // (one wave-uniform branch around the whole tile: a test per element compiles into a
+      // branch per element)
+      if ((t0 + kTile > tok_end) || (t0 < kbeg)) {
   #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (edge) {
+        for (int r = 0; r < 16; ++r) {
           const int tok = t0 + 8 * (r >> 2) + 4 * hl + (r & 3);
           s[r] = (tok < tok_end && tok >= kbeg) ? s[r] : -INFINITY;
         }
-        mx = __builtin_fmaxf(mx, s[r]);
       }
+      float mx = -INFINITY;
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[r]);
       mx = other_half_max(mx) * c_log2;
       // every tile holds an admitted token, so m_new is finite
       const float m_new = __builtin_fmaxf(m_run, mx);
