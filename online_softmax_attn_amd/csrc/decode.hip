@@ -302,7 +302,7 @@ int max_splits_for(int max_seq_len, int window, int split) {
 // (decode_gqa_kernel); smaller ones on the vector units (decode_split_kernel).  Measured on
 // 32 sequences of 1024..8192 tokens, 8 K/V heads: the vector kernel reads 4.0 / 2.3 / 1.2 TB/s
 // at 4 / 8 / 16 heads per group (its work per byte grows with the group), the matrix-core
-// kernel 3.0 TB/s at every group size.
+// kernel 5.0-5.5 TB/s at 8 and 16.
 constexpr int kMfmaGroup = 8;
 
 // Query heads one wave of decode_split_kernel serves: the largest of 4, 2, 1 that divides
@@ -326,9 +326,20 @@ long long waves_per_split(int heads, int kv_heads) {
 // the decode workload (B=32, H=32, lengths up to 8192): 128 tokens 407 us, 256: 390 us,
 // 512: 376 us, 768: 376 us, 1024: 378 us.
 int decode_default_split(int batch, int heads, int kv_heads, int max_seq_len, int window) {
-  constexpr long long kTargetWaves = 8192;
   const long long wave_heads = waves_per_split(heads, kv_heads);
   const long long span = (long long)span_blocks(max_seq_len, window) * kBlock;
+  if (heads / kv_heads >= kMfmaGroup) {
+    // the matrix-core kernel: its waves start with two dependent memory round trips (page
+    // numbers, then the first tiles), so it takes the longest split (at most 1024 tokens)
+    // that still gives 2048 waves.  Measured with 8 K/V heads x 8 query heads, 32 sequences
+    // of 1024..8192 tokens: 128 tokens 4.2 TB/s, 256: 4.6, 512: 4.9, 1024: 5.5.
+    for (int split : {1024, 512, 256, 128}) {
+      const long long waves = (long long)batch * wave_heads * ((span + split - 1) / split);
+      if (waves >= 2048) return split;
+    }
+    return 64;
+  }
+  constexpr long long kTargetWaves = 8192;
   for (int split : {512, 256, 128}) {
     const long long waves = (long long)batch * wave_heads * ((span + split - 1) / split);
     if (waves >= kTargetWaves) return split;
