@@ -34,11 +34,6 @@ constexpr int kBlock = 16;
 #define ATTN_DECODE_DEPTH 2
 #endif
 constexpr int kDepth = ATTN_DECODE_DEPTH;  // blocks requested ahead of the one being consumed
-// A wave serving four or more query heads keeps one block ahead: with two, its registers
-// (the heads' accumulators and queries plus three load buffers) pass 256 and only one wave
-// fits per SIMD; with one it needs 203 and two waves share each SIMD (measured on the
-// grouped decode workload, 8 K/V heads of 4 query heads: 9% faster).
-template <int GQ> constexpr int depth_for() { return GQ >= 4 ? 1 : kDepth; }
 
 struct Partials {  // workspace views; index p = (b * H + h) * max_splits + split
   float* m;        // running max, log2 units
@@ -88,10 +83,11 @@ struct Block {
   uint4 k[4], v[4];  // token 4 i + lane/16, dims 8 (lane%16) .. +7
 };
 
-// One wave per (sequence, K/V head, split, group of GQ query heads).  The GQ query heads
-// share the K/V head, so every block loaded is scored and accumulated GQ times: with
-// grouped heads the cache is read once per K/V head.  Tokens [kbeg, L) are admitted
-// (kbeg > 0 under a window); splits count blocks from the one holding kbeg.
+// One wave per (sequence, K/V head, split, group of GQ query heads sharing that K/V head:
+// every block loaded is scored and accumulated GQ times).  Launched with GQ = 1 (plain
+// multi-head attention); groups of kMfmaGroup or more query heads go to decode_gqa_kernel.
+// Tokens [kbeg, L) are admitted (kbeg > 0 under a window); splits count blocks from the one
+// holding kbeg.
 template <int GQ>
 __global__ __launch_bounds__(64) void decode_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
@@ -201,7 +197,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   };
 
   // software pipeline: kDepth + 1 register buffers, loads kDepth blocks ahead
-  constexpr int kDep = depth_for<GQ>();
+  constexpr int kDep = kDepth;
   Block buf[kDep + 1];
 #pragma unroll
   for (int j = 0; j < kDep; ++j)
@@ -299,24 +295,18 @@ int max_splits_for(int max_seq_len, int window, int split) {
 }
 
 // Groups of at least this many query heads per K/V head run on the matrix cores
-// (decode_gqa_kernel); smaller ones on the vector units (decode_split_kernel).  Measured on
-// 32 sequences of 1024..8192 tokens, 8 K/V heads: the vector kernel reads 4.0 / 2.3 / 1.2 TB/s
-// at 4 / 8 / 16 heads per group (its work per byte grows with the group), the matrix-core
-// kernel 5.0-5.5 TB/s at 8 and 16.
-constexpr int kMfmaGroup = 8;
-
-// Query heads one wave of decode_split_kernel serves: the largest of 4, 2, 1 that divides
-// the group size (groups of kMfmaGroup or more heads never reach this kernel).
-int heads_per_wave(int heads, int kv_heads) {
-  const int G = heads / kv_heads;
-  return G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
-}
+// (decode_gqa_kernel); single heads (plain multi-head attention) on the vector units
+// (decode_split_kernel, one query head per wave).  Measured on 32 sequences of 1024..8192
+// tokens, 8 K/V heads, a 1 GiB write before each call: the matrix-core kernel reads 5.8 /
+// 5.6 / 5.4 / 5.0 TB/s at 2 / 4 / 8 / 16 heads per group, the vector kernel (one wave
+// serving 2 or 4 heads of a group) 5.5 / 4.6 TB/s at 2 / 4.
+constexpr int kMfmaGroup = 2;
 
 // waves per (sequence, split): decode_gqa_kernel takes up to 32 heads of a group per wave
 long long waves_per_split(int heads, int kv_heads) {
   const int G = heads / kv_heads;
   if (G >= kMfmaGroup) return (long long)kv_heads * ((G + 31) / 32);
-  return heads / heads_per_wave(heads, kv_heads);
+  return heads;
 }
 
 }  // namespace
@@ -371,20 +361,11 @@ hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v
                        n_part);
     return hipGetLastError();
   }
-  const int gq = heads_per_wave(heads, kv_heads);
-  const dim3 grid((unsigned)(heads / gq), (unsigned)max_splits, (unsigned)batch);
-  const float c_log2 = scale * ATTN_LOG2E;
-#define ATTN_DECODE_LAUNCH(GQ)                                                                  \
-  hipLaunchKernelGGL(decode_split_kernel<GQ>, grid, dim3(64), 0, stream, q, k_cache, v_cache,   \
-                     block_table, seq_lens, workspace, heads, kv_heads, num_blocks,             \
-                     max_blocks_per_seq, max_seq_len, window, max_splits, split / kBlock,       \
-                     c_log2, n_part)
-  switch (gq) {
-    case 4: ATTN_DECODE_LAUNCH(4); break;
-    case 2: ATTN_DECODE_LAUNCH(2); break;
-    default: ATTN_DECODE_LAUNCH(1); break;
-  }
-#undef ATTN_DECODE_LAUNCH
+  const dim3 grid((unsigned)heads, (unsigned)max_splits, (unsigned)batch);
+  hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(64), 0, stream, q, k_cache, v_cache,
+                     block_table, seq_lens, workspace, heads, kv_heads, num_blocks,
+                     max_blocks_per_seq, max_seq_len, window, max_splits, split / kBlock,
+                     scale * ATTN_LOG2E, n_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(heads, batch), dim3(64), 0, stream, workspace,
