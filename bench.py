@@ -38,7 +38,8 @@ host cores this process may run on, and the GPU clock sampled during the timed s
 --workload long | grouped | window | fp8 | backward | cp | cp-ring | shapes
                   other legs (settled and timed the same way, one JSON line each):
   long      the [1, 32, 32768, 128] causal prefill alone;
-  grouped   causal prefill and decode with 8 K/V heads for the 32 query heads;
+  grouped   causal prefill and decode with 8 K/V heads for the 32 query heads, and the
+            same cache decoded for 64 and 128 query heads (groups of 8 and 16);
   window    causal window 1024: prefill [1, 32, 16384, 128], decode of the decode workload;
   fp8       causal prefill [4, 32, 2048, 128] on E4M3 operands (attn_fwd_fp8), the block
             quantisation (attn_quantize_fp8) timed apart; roofline: dense fp8 MFMA peak;
@@ -141,10 +142,12 @@ def host_cores():
 
 # --------------------------------------------------------------------------- timing helpers
 class ClockSampler:
-    """GPU shader-clock samples (MHz) taken every ~5 ms on a side thread while phases run;
+    """GPU shader-clock readings (MHz) polled every ~5 ms on a side thread while phases run;
     `mark(name)` labels what runs from then on.  The source is the SMI library's GPU
     metrics table (mean of the per-XCD current GFX clocks), read through the handle torch
-    keeps for it."""
+    keeps for it.  The firmware refreshes that table about once per second, so only the
+    readings with a new firmware timestamp are kept: each is the clock at one refresh, and
+    a phase shorter than a second may hold none."""
 
     def __init__(self):
         self.samples = []          # (phase, t, MHz)
@@ -162,11 +165,12 @@ class ClockSampler:
 
         def read():
             m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            ts = m.get("firmware_timestamp")
             xs = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and x > 0]
             if xs:
-                return sum(xs) / len(xs)
+                return sum(xs) / len(xs), ts
             x = m.get("current_gfxclk")
-            return float(x) if isinstance(x, (int, float)) else 0.0
+            return (float(x) if isinstance(x, (int, float)) else 0.0), ts
 
         read()
         return read
@@ -180,13 +184,16 @@ class ClockSampler:
 
         def run():
             t0 = time.perf_counter()
+            last = None
             while not self._stop.is_set():
                 try:
-                    mhz = float(self._read())
+                    mhz, ts = self._read()
                 except Exception as e:
                     self.error = f"{type(e).__name__}: {e}"[:200]
                     return
-                self.samples.append((self.phase, time.perf_counter() - t0, mhz))
+                if ts != last:  # a refresh of the table
+                    last = ts
+                    self.samples.append((self.phase, time.perf_counter() - t0, float(mhz)))
                 self._stop.wait(0.005)
 
         self._t = threading.Thread(target=run, daemon=True)
@@ -203,11 +210,12 @@ class ClockSampler:
 
     def summary(self, phases):
         vals = [m for p, _, m in self.samples if p in phases and m > 0]
-        out = {"source": "amdsmi GPU metrics, mean of the per-XCD current GFX clocks, ~5 ms "
-                         "period", "phases": sorted(phases), "samples": len(vals)}
+        out = {"source": "amdsmi GPU metrics, mean of the per-XCD current GFX clocks, one "
+                         "reading per refresh of the table (about once per second)",
+               "phases": sorted(phases), "readings": len(vals)}
         if vals:
             out.update(median_mhz=round(statistics.median(vals), 1), min_mhz=round(min(vals), 1),
-                       max_mhz=round(max(vals), 1), distinct=len(set(vals)))
+                       max_mhz=round(max(vals), 1))
         if self.error:
             out["error"] = self.error
         return out
@@ -621,15 +629,35 @@ def bench_two_legs(args, attn, workloads, torch):
 
         fns.append(decode)
         dec = (decode, flush)
-    settle_ms, _ = settle(fns, args.settle_ms / 1e3)
+        groups = []  # grouped workload: the same cache under 8 and 16 query heads per K/V head
+        if args.workload == "grouped":
+            gq = torch.Generator().manual_seed(45)
+            for Hg in (64, 128):
+                qg = torch.randn(32, Hg, 128, generator=gq).to(torch.bfloat16).to(dev)
+                og = torch.empty_like(qg)
+                wsg = torch.empty(attn.attn_decode_workspace_bytes(32, Hg, 128, pw.max_seq_len,
+                                                                   kv_heads=kv_heads),
+                                  dtype=torch.uint8, device=dev)
+
+                def dec_g(qg=qg, og=og, wsg=wsg):
+                    attn.attn_decode_paged(qg, kc, vc, tbl, lens, max_seq_len=pw.max_seq_len,
+                                           out=og, workspace=wsg)
+
+                groups.append((Hg // kv_heads, dec_g, qg.numel()))
+                fns.append(dec_g)
+    settle_ms, rounds = settle(fns, args.settle_ms / 1e3)
     for _ in range(args.warmup):
         for f in fns:
             f()
     torch.cuda.synchronize()
+    # launches of each kernel before the timed ones (settle rounds and warm-up steps call
+    # every function once; a burst starts with one untimed launch)
+    before = rounds + args.warmup
     t0 = time.perf_counter()
     pre_avg = burst_ms(prefill, args.steps)
     if dec:
         dec_ms = flushed_times(dec[0], dec[1], args.steps)
+        group_ms = [(G, flushed_times(fn, dec[1], args.steps), nq) for G, fn, nq in groups]
     wall = time.perf_counter() - t0
     pre_stats = burst_stats(prefill, 50, 2 if n > 8192 else 5)
     tf = flops_rate(flops, pre_avg)
@@ -645,6 +673,7 @@ def bench_two_legs(args, attn, workloads, torch):
         "prefill": dict({"ms_avg": round(pre_avg, 5), "tflops": round(tf, 2), "flops": flops},
                         **pre_stats),
         "roofline": roofline_mfma(tf),
+        "trace_index": {"fwd_bf16_kernel": [before + 1, args.steps]},
     }
     if dec:
         avg = sum(dec_ms) / len(dec_ms)
@@ -654,6 +683,23 @@ def bench_two_legs(args, attn, workloads, torch):
                                 **stats(dec_ms, f"{len(dec_ms)} calls, each after a 1 GiB "
                                                 "scratch write"),
                                 roofline=roofline_hbm(gbs))
+        result["decode"]["heads_per_kv_head"] = 32 // kv_heads
+        kern = "decode_gqa_kernel" if kv_heads < 32 else "decode_split_kernel"
+        n_dec = 1 + len(group_ms)
+        for i, tag in enumerate(["H32"] + [f"H{G * kv_heads}" for G, _, _ in group_ms]):
+            for kname in (kern, "decode_merge_kernel"):
+                result["trace_index"][f"{kname}#{tag}"] = [n_dec * before + i * args.steps,
+                                                           args.steps]
+        for G, ms, nq in group_ms:
+            avg = sum(ms) / len(ms)
+            gbytes = dbytes - 2 * pw.q.numel() * 2 + 2 * nq * 2  # the same cache, its own q, o
+            gbs = gbytes / (avg * 1e-3) / 1e9
+            result[f"decode_group{G}"] = dict(
+                {"value": round(gbs, 1), "unit": "GB/s", "ms_avg": round(avg, 5),
+                 "config": f"paged decode B=32 H={G * kv_heads} H_kv={kv_heads} d=128, the same "
+                           "cache and lengths", "bytes": gbytes},
+                **stats(ms, f"{len(ms)} calls, each after a 1 GiB scratch write"),
+                roofline=roofline_hbm(gbs))
     print(json.dumps(result))
 
 
@@ -671,7 +717,7 @@ def bench_backward(args, attn, workloads, torch):
     def step():
         attn.attn_bwd(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    settle_ms, _ = settle([step], args.settle_ms / 1e3)
+    settle_ms, rounds = settle([step], args.settle_ms / 1e3)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -679,6 +725,7 @@ def bench_backward(args, attn, workloads, torch):
     ms = burst_ms(step, args.steps)
     wall = time.perf_counter() - t0
     st = burst_stats(step, 50, 2)
+    first = rounds + args.warmup + 1
     flops = 2.5 * causal_flops(B, H, n, d)
     tf = flops_rate(flops, ms)
     print(json.dumps({
@@ -689,7 +736,9 @@ def bench_backward(args, attn, workloads, torch):
         "data": "synthetic (seeded N(0,1) Q/K/V/dO)",
         "config": {"workload": "causal backward B=4 H=32 n=2048 d=128 bf16 -> fp32 grads"},
         "settle": {"ms": round(settle_ms, 1)},
-        "roofline": roofline_mfma(tf), "ms_avg": round(ms, 5), **st}))
+        "roofline": roofline_mfma(tf), "ms_avg": round(ms, 5), **st,
+        "trace_index": {"bwd_dq_kernel": [first, args.steps],
+                        "bwd_dkdv_kernel": [first, args.steps]}}))
 
 
 def bench_fp8(args, attn, workloads, torch):
@@ -718,7 +767,7 @@ def bench_fp8(args, attn, workloads, torch):
         cyc[0] += 1
         step(cyc[0])
 
-    settle_ms, _ = settle([step, quantize], args.settle_ms / 1e3)
+    settle_ms, rounds = settle([step, quantize], args.settle_ms / 1e3)
     for _ in range(args.warmup):
         quantize()
         step()
@@ -742,7 +791,8 @@ def bench_fp8(args, attn, workloads, torch):
         "roofline": roofline_mfma(tf, PEAK_FP8_TFLOPS),
         "ms_avg": round(ms, 5), **st, "cold_ms_avg": round(cold_ms, 5),
         "cold_tflops": round(flops_rate(flops, cold_ms), 2), "cold_input_sets": n_sets,
-        "quantize_ms_avg": round(q_ms, 5)}))
+        "quantize_ms_avg": round(q_ms, 5),
+        "trace_index": {"fwd_fp8_kernel": [rounds + args.warmup + 1, args.steps]}}))
 
 
 def bench_cp(args, attn, workloads, torch):
@@ -788,13 +838,17 @@ def bench_cp(args, attn, workloads, torch):
             else:
                 attn.attn_fwd_chunk(Qc[i], k, v, i * c, causal=True, out=outs[i], lse=out_lse[i])
 
-    settle_ms, _ = settle([step], args.settle_ms / 1e3)
+    settle_ms, rounds = settle([step], args.settle_ms / 1e3)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ms = burst_ms(step, args.steps)
     wall = time.perf_counter() - t0
+    per_step = sum(i + 1 for i in owned) if ring else len(owned)  # forward launches per step
+    index = {"fwd_bf16_kernel": [(rounds + args.warmup + 1) * per_step, args.steps * per_step]}
+    if ring:
+        index["merge_kernel"] = [(rounds + args.warmup + 1) * len(owned), args.steps * len(owned)]
     full = 4.0 * d * B * H * c * c                  # an unmasked chunk pair
     diag = 4.0 * d * B * H * c * (c + 1) / 2        # a causal diagonal chunk
     n_full = sum(owned)
@@ -813,7 +867,7 @@ def bench_cp(args, attn, workloads, torch):
                                f"{G} devices (zig-zag); device {g_dev}: query chunks {owned}; "
                                f"{form}; the K/V exchange itself not included"},
         "settle": {"ms": round(settle_ms, 1)},
-        "roofline": roofline_mfma(tf), "ms_avg": round(ms, 5)}))
+        "roofline": roofline_mfma(tf), "ms_avg": round(ms, 5), "trace_index": index}))
 
 
 def bench_shapes(args, attn, workloads, torch):
@@ -958,6 +1012,24 @@ def record_traffic(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
+def summarize_trace_legs(rows, ti):
+    """Summary for the other legs: `trace_index` maps "kernel[#tag]" to [first, count], the
+    timed launches among those whose name contains `kernel`, in launch order."""
+    out = ["| kernel (timed launches) | launches in the run | timed | avg (us) | median (us) | "
+           "min (us) | max (us) |", "|---|---|---|---|---|---|---|"]
+    for key, (first, count) in ti.items():
+        kname = key.split("#")[0]
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+             if kname in r["Kernel_Name"]]
+        timed = d[first:first + count]
+        if not timed:
+            out.append(f"| {key} | {len(d)} | 0 | | | | |")
+            continue
+        out.append(f"| {key} | {len(d)} | {len(timed)} | {sum(timed) / len(timed):.2f} | "
+                   f"{statistics.median(timed):.2f} | {min(timed):.2f} | {max(timed):.2f} |")
+    print("\n".join(out))
+
+
 def summarize_trace(trace_csv, line_file):
     """Markdown summary of a rocprofv3 kernel trace of a default run, checked against the
     run's JSON line: the average duration over exactly the timed launches of each leg."""
@@ -996,6 +1068,8 @@ def summarize_trace(trace_csv, line_file):
         by_kind.setdefault(kind, []).append(dur)
     K = int(line["steps"])
     ti = line["trace_index"]
+    if all(isinstance(x, list) for x in ti.values()):
+        return summarize_trace_legs(rows, ti)
     out = ["| kernel | launches | avg over all (us) | avg over the timed launches (us) | line (us) |",
            "|---|---|---|---|---|"]
 

@@ -104,3 +104,27 @@ def test_summarize_trace_averages_exactly_the_timed_launches(tmp_path, capsys):
     assert "| 160.00 | 160.00 |" in out          # (150 + 170) / 2 us, line 0.16 ms
     assert "| 8100.00 | 8100.00 |" in out        # (8000 + 8200) / 2 us
     assert "| 390.00 |" in out                   # decode split + merge: (380+390)/2 + 5
+
+
+def test_summarize_trace_legs_takes_the_indexed_launches(tmp_path, capsys):
+    # one kernel name shared by two timed groups (tags), with untimed launches before each
+    rows, t = [], 0
+    for name, dur in [("void decode_gqa_kernel(...)", 1_000)] * 2 + \
+                     [("void decode_gqa_kernel(...)", 100_000), ("void decode_gqa_kernel(...)", 120_000),
+                      ("void decode_gqa_kernel(...)", 200_000), ("void decode_gqa_kernel(...)", 220_000),
+                      ("void bwd_dq_kernel(...)", 50_000)]:
+        rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur})
+        t += dur + 10
+    with open(tmp_path / "trace.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=list(rows[0]))
+        wr.writeheader()
+        wr.writerows(rows)
+    line = {"metric": "m", "steps": 2,
+            "trace_index": {"decode_gqa_kernel#H32": [2, 2], "decode_gqa_kernel#H64": [4, 2],
+                            "bwd_dq_kernel": [0, 1]}}
+    (tmp_path / "line.log").write_text(json.dumps(line) + "\n")
+    bench.summarize_trace(str(tmp_path / "trace.csv"), str(tmp_path / "line.log"))
+    out = capsys.readouterr().out
+    assert "| decode_gqa_kernel#H32 | 6 | 2 | 110.00 |" in out
+    assert "| decode_gqa_kernel#H64 | 6 | 2 | 210.00 |" in out
+    assert "| bwd_dq_kernel | 1 | 1 | 50.00 |" in out
