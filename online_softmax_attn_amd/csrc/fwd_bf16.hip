@@ -350,6 +350,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     if (t + 2 < n_tiles) issue_k(t + 2, Kf);
     issue_v(t + 1, Vf);
     bf16x8 pop[4];
+    // Two waves share each SIMD (one from each of the CU's two workgroups).  The score and
+    // weight phase, whose exps and FMAs leave the matrix core idle between its products,
+    // issues at raised priority; a wave in its P V phase (back-to-back products) then fills
+    // the matrix core in those gaps instead of competing with it for issue.  [4,32,2048,128]
+    // 137.4 -> 135.5 us, [1,32,32768,128] 7575 -> 7075 us.
+    __builtin_amdgcn_s_setprio(1);
     compute_s(nxt, Kr);
     const float psum = weights(cur, pop);
     __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
@@ -360,6 +366,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
     }
     checked_weights(cur, pop, psum);
+    __builtin_amdgcn_s_setprio(0);
     pv(Vr, pop);
     __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 8, 1);
 #pragma unroll
@@ -377,7 +384,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   auto step_last = [&](int t, Tile& cur, const bf16* Vr) __attribute__((always_inline)) {
     if (t < wave_tiles) {
       bf16x8 pop[4];
+      __builtin_amdgcn_s_setprio(1);
       checked_weights(cur, pop, weights(cur, pop));
+      __builtin_amdgcn_s_setprio(0);
       pv(Vr, pop);
     }
   };
@@ -397,9 +406,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     Tile ta, tb;
+    __builtin_amdgcn_s_setprio(1);
     compute_s(ta, k0);
     if (need_mask(t0)) apply_mask(ta, t0 * kBN);
     raise_ref(row_max(ta));
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // every wave is done with K(t0) before K(t0+2) overwrites its buffer
 
     for (int t = t0; t < t_last; t += 2) {
