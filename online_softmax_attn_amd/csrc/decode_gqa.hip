@@ -200,17 +200,23 @@ __global__ __launch_bounds__(64) void decode_gqa_kernel(
   #pragma unroll
       for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[r]);
       mx = other_half_max(mx) * c_log2;
-      // every tile holds an admitted token, so m_new is finite
-      const float m_new = __builtin_fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from the empty state
+      // The reference m_run follows the running maximum lazily: it is raised (l and u
+      // rescaled by 2^(old - new)) only when a score exceeds it by more than 2^8, so weights
+      // stay <= 2^8 and the rescale is mostly skipped; on the first tile (l = u = 0) it is
+      // just set.  Every tile holds an admitted token, so mx is finite.
+      if (t == 0) {
+        m_run = mx;
+      } else if (__any(mx > m_run + 8.0f)) {
+        const float m_new = __builtin_fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
   #pragma unroll
         for (int db = 0; db < 4; ++db)
   #pragma unroll
           for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        m_run = m_new;
       }
-      m_run = m_new;
+      const float m_new = m_run;
       // ---- P^T operand (bf16) and the normaliser from the same rounded weights
       bf16x8 pop[2];
   #pragma unroll
