@@ -79,6 +79,9 @@ __device__ __forceinline__ float other_half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// s_waitcnt immediate (gfx9 encoding): vector-memory count <= n, the other counts unconstrained
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 
@@ -403,15 +406,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     issue_k(t0, k0);
     issue_v(t0, v0);
     if (t0 + 1 < n_tiles) issue_k(t0 + 1, k1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // Q and K(t0) have landed once at most the later fills (4 instructions each) are in flight
+    if (t0 + 1 < n_tiles)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+    // a bare barrier: __syncthreads() would also wait for the fills still in flight
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     Tile ta, tb;
     __builtin_amdgcn_s_setprio(1);
     compute_s(ta, k0);
     if (need_mask(t0)) apply_mask(ta, t0 * kBN);
     raise_ref(row_max(ta));
     __builtin_amdgcn_s_setprio(0);
-    __syncthreads();  // every wave is done with K(t0) before K(t0+2) overwrites its buffer
+    __builtin_amdgcn_s_waitcnt(0);  // V(t0) and K(t0+1) have landed
+    __syncthreads();  // ... for every wave; every wave is done with K(t0) before K(t0+2) overwrites it
 
     for (int t = t0; t < t_last; t += 2) {
       step(t, ta, tb, k0, v1, k1, v0);
