@@ -35,7 +35,7 @@ entries read.  `roofline` describes the causal prefill kernel against the bf16 d
 peak; `decode.roofline` the decode against HBM.  `env` records versions, the device, the
 host cores this process may run on, and the GPU clock sampled during the timed steps.
 
---workload long | grouped | window | fp8 | backward | cp | cp-ring | shapes
+--workload long | grouped | window | fp8 | backward | cp | cp-ring | shapes | ceilings
                   other legs (settled and timed the same way, one JSON line each):
   long      the [1, 32, 32768, 128] causal prefill alone;
   grouped   causal prefill and decode with 8 K/V heads for the 32 query heads, and the
@@ -50,7 +50,10 @@ host cores this process may run on, and the GPU clock sampled during the timed s
   cp-ring   the same share as a ring delivers K/V chunks: attn_fwd per chunk pair, then
             attn_merge;
   shapes    throughput across shapes (prefill, fp32, fp8, backward, decode), one JSON line
-            per shape, under sustained load.
+            per shape, under sustained load;
+  ceilings  the device's own ceilings from the library's probe kernels (include/attn_probe.h):
+            dense bf16 and fp8 MFMA rate, v_exp_f32 rate, HBM read bandwidth streamed and in
+            4 KiB pages in random order, each with its checksum verified.
 --profile-pass    one 1 GiB device copy, one causal prefill and one decode, then exit (the
                   command the rocprofv3 counter runs wrap).
 --record-traffic FETCH_CSV WRITE_CSV
@@ -974,6 +977,98 @@ def bench_shapes(args, attn, workloads, torch):
 
 
 # --------------------------------------------------------------------------- profiles
+def bench_ceilings(args, attn, workloads, torch):
+    """The device's own ceilings, measured by the probe kernels of the library
+    (include/attn_probe.h), each settled for about a second and then timed in 10 bursts of
+    3 back-to-back launches (median): dense matrix-core rate in bf16 and fp8 (blocks of
+    ones, four accumulation chains per wave, two workgroups per CU), v_exp_f32 rate (eight
+    chains x <- 2^(-x) per lane), and HBM reads of a 2 GiB buffer, streamed and as 4 KiB
+    pages in a seeded random order (the paged decode's access).  Every probe's checksum is
+    verified against the value the work must produce."""
+    from online_softmax_attn_amd import binding as b
+
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    clock = ClockSampler().start()
+    checks = {}
+    line = {}
+
+    def timed(name, fn, work, unit_scale):
+        clock.mark(name)
+        settle([fn], 1.0)
+        ms = [burst_ms(fn, 3) for _ in range(10)]
+        med = statistics.median(ms)
+        clock.mark("idle")
+        rate = work / (med * 1e-3) / unit_scale
+        return rate, stats(ms, "10 bursts of 3 back-to-back launches (burst time / 3)")
+
+    # matrix cores: per wave `iters` rounds of 4 products; flops per product 2*32*32*k
+    blocks = 16 * cus
+    mf = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+    for key, fp8, iters, k, peak in (("mfma_bf16", 0, 4096, 16, PEAK_BF16_TFLOPS),
+                                     ("mfma_fp8", 1, 2048, 64, PEAK_FP8_TFLOPS)):
+        flops = blocks * 4 * iters * 4 * 2 * 32 * 32 * k
+        fn = (lambda fp8=fp8, iters=iters: b.attn_probe_mfma(fp8, blocks, iters, out=mf))
+        tf, st = timed(key, fn, flops, 1e12)
+        torch.cuda.synchronize()
+        checks[key] = bool(torch.all(mf == float(16 * k * iters * 4)).item())
+        line[key] = {"tflops": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4),
+                     "flops_per_launch": flops, **st,
+                     "clock": clock.summary({key})}
+
+    # transcendental rate
+    eb, iters = 16 * cus, 4096
+    eo = torch.empty(eb * b.ATTN_PROBE_THREADS, dtype=torch.float32, device=dev)
+    exps = eb * b.ATTN_PROBE_THREADS * iters * 8
+    rate, st = timed("exp", lambda: b.attn_probe_exp(eb, iters, out=eo), exps, 1e9)
+    torch.cuda.synchronize()
+    fixed = 0.641185744504986  # x = 2^(-x)
+    checks["exp"] = bool(torch.all((eo - 8 * fixed).abs() < 1e-4).item())
+    line["exp"] = {"gexp_per_s": round(rate, 1), "exps_per_launch": exps, **st,
+                   "clock": clock.summary({"exp"})}
+
+    # HBM reads: 2 GiB of seeded words, streamed and as pages in a seeded random order
+    nbytes = 2 << 30
+    g = torch.Generator(device=dev)
+    g.manual_seed(20260924)
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev,
+                        generator=g)
+    want = int(sum(int(c.to(torch.int64).sum().item()) for c in src.split(1 << 26))) % 2**32
+    rb = 8 * cus
+    ro = torch.empty(rb * b.ATTN_PROBE_THREADS, dtype=torch.int32, device=dev)
+    gbs, st = timed("hbm_stream", lambda: b.attn_probe_read(src, rb, out=ro), nbytes, 1e9)
+    torch.cuda.synchronize()
+    checks["hbm_stream"] = int(ro.to(torch.int64).sum().item()) % 2**32 == want
+    line["hbm_stream"] = {"gbs": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                          "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes, **st}
+    pages = nbytes // 4096
+    gp = torch.Generator().manual_seed(4)
+    order = torch.randperm(pages, generator=gp).to(torch.int32).to(dev)
+    gbs, st = timed("hbm_pages_4k", lambda: b.attn_probe_read_pages(src, order, rb, out=ro),
+                    nbytes, 1e9)
+    torch.cuda.synchronize()
+    checks["hbm_pages_4k"] = int(ro.to(torch.int64).sum().item()) % 2**32 == want
+    line["hbm_pages_4k"] = {"gbs": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                            "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+                            "pages": pages, **st}
+    clock.stop()
+
+    bf = line["mfma_bf16"]
+    out = {"metric": "machine ceilings (probe kernels of libattn.so): dense bf16 MFMA TFLOP/s",
+           "value": bf["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": 10,
+           "warmup": 0, "ms_per_step": bf["median_ms"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (blocks of ones; seeded random words for the reads)",
+           "config": {"workload": "ceilings: matrix-core, exp and HBM-read probes",
+                      "compute_units": cus},
+           "roofline": roofline_mfma(bf["tflops"]), **line, "checksums": checks,
+           "env": env_info()}
+    print(json.dumps(out), flush=True)
+    if not all(checks.values()):
+        print(f"probe checksum mismatch: {checks}", file=sys.stderr)
+        sys.exit(1)
+
+
 def record_traffic(fetch_csv, write_csv):
     """profiles/traffic.json from FETCH_SIZE / WRITE_SIZE runs of --profile-pass."""
     import csv
@@ -1111,7 +1206,7 @@ def main():
     # before the warm-up steps, whatever --warmup is
     ap.add_argument("--settle-ms", type=float, default=400.0)
     ap.add_argument("--workload", choices=["prefill", "long", "backward", "grouped", "window",
-                                           "fp8", "cp", "cp-ring", "shapes"],
+                                           "fp8", "cp", "cp-ring", "shapes", "ceilings"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -1132,7 +1227,8 @@ def main():
     attn.lib()
     legs = {"prefill": bench_default, "long": bench_two_legs, "grouped": bench_two_legs,
             "window": bench_two_legs, "backward": bench_backward, "fp8": bench_fp8,
-            "cp": bench_cp, "cp-ring": bench_cp, "shapes": bench_shapes}
+            "cp": bench_cp, "cp-ring": bench_cp, "shapes": bench_shapes,
+            "ceilings": bench_ceilings}
     legs[args.workload](args, attn, workloads, torch)
 
 

@@ -12,6 +12,10 @@ Entry points mirror the C ABI in include/attn.h:
     attn_fwd_fp8                  prefill on E4M3 operands (bf16 output)
     attn_merge                    join results over disjoint key sets by their lse
     attn_status_str, attn_abi_version
+
+Measurement kernels (include/attn_probe.h: matrix-core, exp and HBM-read rates of the
+device) are in `binding` under their C names (attn_probe_mfma, attn_probe_exp,
+attn_probe_read, attn_probe_read_pages); `python bench.py --workload ceilings` runs them.
 """
 
 from .binding import (

@@ -55,6 +55,14 @@ SIGNATURES = {
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
 }
+# the measurement kernels, exactly the declarations of include/attn_probe.h
+PROBE_SIGNATURES = {
+    "attn_probe_mfma": (_I, [_I, _I, _I, _P, _P]),
+    "attn_probe_exp": (_I, [_I, _I, _P, _P]),
+    "attn_probe_read": (_I, [_P, ctypes.c_size_t, _I, _P, _P]),
+    "attn_probe_read_pages": (_I, [_P, _I, _P, _I, _I, _P, _P]),
+}
+ATTN_PROBE_THREADS = 256
 
 _lib = None
 
@@ -74,7 +82,7 @@ def lib() -> ctypes.CDLL:
                 f"{LIB_PATH} is missing: build it with `python -m online_softmax_attn_amd.build` "
                 "(there is no fallback implementation)")
         handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
+        for name, (res, args) in {**SIGNATURES, **PROBE_SIGNATURES}.items():
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
@@ -499,3 +507,68 @@ def attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, *, causal=False, scale=
     if st != ATTN_OK:
         raise AttnError("attn_fwd_fp8", st)
     return (out, lse) if return_lse else out
+
+
+# ---- measurement kernels (include/attn_probe.h)
+
+def _raise(func, status):
+    if status != ATTN_OK:
+        raise AttnError(func, status)
+
+
+def _probe_out(n, dtype, device, out):
+    if out is None:
+        return torch.empty(n, dtype=dtype, device=device)
+    _check_dev("out", out, dtype)
+    if out.numel() < n:
+        raise ValueError(f"out holds {out.numel()} values, the probe writes {n}")
+    return out
+
+
+@_on_stream
+def attn_probe_mfma(fp8, blocks, iters, *, device="cuda", out=None, stream=None):
+    """Matrix-core rate probe; returns out (float32[blocks * 4], each 1024 * iters for bf16,
+    4096 * iters for fp8)."""
+    out = _probe_out(blocks * (ATTN_PROBE_THREADS // 64), torch.float32, device, out)
+    _raise("attn_probe_mfma", lib().attn_probe_mfma(int(bool(fp8)), blocks, iters,
+                                                    _P(out.data_ptr()), _stream(stream)))
+    return out
+
+
+@_on_stream
+def attn_probe_exp(blocks, iters, *, device="cuda", out=None, stream=None):
+    """v_exp_f32 rate probe; returns out (float32[blocks * 256])."""
+    out = _probe_out(blocks * ATTN_PROBE_THREADS, torch.float32, device, out)
+    _raise("attn_probe_exp", lib().attn_probe_exp(blocks, iters, _P(out.data_ptr()),
+                                                  _stream(stream)))
+    return out
+
+
+@_on_stream
+def attn_probe_read(src, blocks, *, out=None, stream=None):
+    """Streaming-read probe over the bytes of a contiguous device tensor (a multiple of
+    4096 bytes); returns the per-thread wrapping word sums (int32 view of uint32)."""
+    if not (src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous device tensor")
+    out = _probe_out(blocks * ATTN_PROBE_THREADS, torch.int32, src.device, out)
+    nbytes = src.numel() * src.element_size()
+    _raise("attn_probe_read", lib().attn_probe_read(_P(src.data_ptr()), nbytes, blocks,
+                                                      _P(out.data_ptr()), _stream(stream)))
+    return out
+
+
+@_on_stream
+def attn_probe_read_pages(pool, order, blocks, *, out=None, stream=None):
+    """Paged-read probe: the 4 KiB pages of `pool` (contiguous device tensor) in the order
+    of `order` (device int32); returns the per-thread wrapping word sums."""
+    if not (pool.is_cuda and pool.is_contiguous()):
+        raise ValueError("pool must be a contiguous device tensor")
+    _check_dev("order", order, torch.int32)
+    nbytes = pool.numel() * pool.element_size()
+    if nbytes % 4096:
+        raise ValueError("pool must hold whole 4 KiB pages")
+    out = _probe_out(blocks * ATTN_PROBE_THREADS, torch.int32, pool.device, out)
+    _raise("attn_probe_read_pages",
+           lib().attn_probe_read_pages(_P(pool.data_ptr()), nbytes // 4096, _P(order.data_ptr()),
+                                       order.numel(), blocks, _P(out.data_ptr()), _stream(stream)))
+    return out

@@ -19,8 +19,11 @@ INVALID, UNSUPPORTED, WORKSPACE = (binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UN
                                    binding.ATTN_ERR_WORKSPACE)
 
 
-def declared_functions():
-    text = open(HEADER).read()
+PROBE_HEADER = os.path.join(ROOT, "include", "attn_probe.h")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
@@ -31,6 +34,36 @@ def test_library_exports_every_declared_function():
     lib = attn.lib()
     for name in names:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_library_exports_every_probe_function():
+    names = declared_functions(PROBE_HEADER)
+    assert set(names) == set(binding.PROBE_SIGNATURES), names
+    lib = attn.lib()
+    for name in names:
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+@pytest.mark.parametrize("call", [
+    lambda L: L.attn_probe_mfma(0, 1, 1, None, None),
+    lambda L: L.attn_probe_mfma(2, 1, 1, FAKE, None),
+    lambda L: L.attn_probe_mfma(0, 0, 1, FAKE, None),
+    lambda L: L.attn_probe_mfma(1, 1, 0, FAKE, None),
+    lambda L: L.attn_probe_mfma(0, 1, 16385, FAKE, None),
+    lambda L: L.attn_probe_exp(0, 1, FAKE, None),
+    lambda L: L.attn_probe_exp(1, -1, FAKE, None),
+    lambda L: L.attn_probe_exp(1, 1, None, None),
+    lambda L: L.attn_probe_read(None, 4096, 1, FAKE, None),
+    lambda L: L.attn_probe_read(FAKE, 0, 1, FAKE, None),
+    lambda L: L.attn_probe_read(FAKE, 4100, 1, FAKE, None),
+    lambda L: L.attn_probe_read(FAKE, 4096, 0, FAKE, None),
+    lambda L: L.attn_probe_read_pages(FAKE, 8, None, 8, 1, FAKE, None),
+    lambda L: L.attn_probe_read_pages(FAKE, 0, FAKE, 8, 1, FAKE, None),
+    lambda L: L.attn_probe_read_pages(FAKE, 8, FAKE, 0, 1, FAKE, None),
+    lambda L: L.attn_probe_read_pages(None, 8, FAKE, 8, 1, FAKE, None),
+])
+def test_probe_validation(call):
+    assert call(attn.lib()) == INVALID
 
 
 def test_abi_version_matches_header():
