@@ -981,10 +981,10 @@ def bench_ceilings(args, attn, workloads, torch):
     """The device's own ceilings, measured by the probe kernels of the library
     (include/attn_probe.h), each settled for about a second and then timed in 10 bursts of
     3 back-to-back launches (median): dense matrix-core rate in bf16 and fp8 (blocks of
-    ones, four accumulation chains per wave, two workgroups per CU), v_exp_f32 rate (eight
-    chains x <- 2^(-x) per lane), and HBM reads of a 2 GiB buffer, streamed and as 4 KiB
-    pages in a seeded random order (the paged decode's access).  Every probe's checksum is
-    verified against the value the work must produce."""
+    ones times blocks of twos, two accumulation chains per wave, two workgroups per CU),
+    v_exp_f32 rate (eight chains x <- 2^(-x) per lane), and HBM reads of a 2 GiB buffer,
+    streamed and as 4 KiB pages in a seeded random order (the paged decode's access).
+    Every probe's checksum is verified against the value the work must produce."""
     from online_softmax_attn_amd import binding as b
 
     dev = torch.device("cuda:0")
@@ -1005,13 +1005,13 @@ def bench_ceilings(args, attn, workloads, torch):
     # matrix cores: per wave `iters` rounds of 4 products; flops per product 2*32*32*k
     blocks = 16 * cus
     mf = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
-    for key, fp8, iters, k, peak in (("mfma_bf16", 0, 4096, 16, PEAK_BF16_TFLOPS),
-                                     ("mfma_fp8", 1, 2048, 64, PEAK_FP8_TFLOPS)):
-        flops = blocks * 4 * iters * 4 * 2 * 32 * 32 * k
+    for key, fp8, iters, k, peak in (("mfma_bf16", 0, 8192, 16, PEAK_BF16_TFLOPS),
+                                     ("mfma_fp8", 1, 4096, 64, PEAK_FP8_TFLOPS)):
+        flops = blocks * 4 * iters * 2 * 2 * 32 * 32 * k
         fn = (lambda fp8=fp8, iters=iters: b.attn_probe_mfma(fp8, blocks, iters, out=mf))
         tf, st = timed(key, fn, flops, 1e12)
         torch.cuda.synchronize()
-        checks[key] = bool(torch.all(mf == float(16 * k * iters * 4)).item())
+        checks[key] = bool(torch.all(mf == float(64 * k * iters)).item())
         line[key] = {"tflops": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4),
                      "flops_per_launch": flops, **st,
                      "clock": clock.summary({key})}
@@ -1058,7 +1058,7 @@ def bench_ceilings(args, attn, workloads, torch):
            "value": bf["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": 10,
            "warmup": 0, "ms_per_step": bf["median_ms"], "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic (blocks of ones; seeded random words for the reads)",
+           "data": "synthetic (blocks of ones and twos; seeded random words for the reads)",
            "config": {"workload": "ceilings: matrix-core, exp and HBM-read probes",
                       "compute_units": cus},
            "roofline": roofline_mfma(bf["tflops"]), **line, "checksums": checks,

@@ -17,9 +17,10 @@
  * `stream`, nothing allocated, host-visible arguments checked first, ATTN_ERR_INVALID for a
  * null pointer or a size <= 0).  Each kernel writes a checksum the caller can verify, so
  * the work cannot be elided:
- *   - the matrix-core probes multiply blocks of ones: every accumulator element ends at
- *     16 * iters (bf16) or 64 * iters (fp8), and `out[w]` for each wave w of the grid
- *     holds the sum over one lane's 64 accumulator values, 1024 * iters or 4096 * iters;
+ *   - the matrix-core probes multiply blocks of ones by blocks of twos: every accumulator
+ *     element ends at 32 * iters (bf16) or 128 * iters (fp8), and `out[w]` for each wave w
+ *     of the grid holds the sum over one lane's 32 accumulator values, 1024 * iters or
+ *     4096 * iters;
  *   - the exp probe iterates x <- 2^(-x) from 0.5 in 8 chains per lane (each x converges
  *     to the fixed point 0.6412); `out[t]` for each thread t holds the sum of its 8 values;
  *   - the read probes write, per thread of the grid, the 32-bit wrapping sum of the 32-bit
@@ -41,10 +42,10 @@ extern "C" {
 #define ATTN_PROBE_THREADS 256
 
 /*
- * attn_probe_mfma — `blocks` workgroups, each wave running `iters` rounds of four
+ * attn_probe_mfma — `blocks` workgroups, each wave running `iters` rounds of two
  * independent accumulation chains of the matrix-core product (fp8 = 0: bf16 32x32x16;
  * fp8 = 1: E4M3 32x32x64), two workgroups per CU.  Flops per call:
- * blocks * 4 * iters * 4 * 2 * 32 * 32 * (16 or 64).
+ * blocks * 4 * iters * 2 * 2 * 32 * 32 * (16 or 64).
  * out: float[blocks * 4].  iters <= 16384 (the checksum stays exact in fp32).
  */
 attn_status attn_probe_mfma(int fp8, int blocks, int iters, float* out, void* stream);

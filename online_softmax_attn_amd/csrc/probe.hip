@@ -12,33 +12,42 @@ constexpr int kThreads = ATTN_PROBE_THREADS;
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// Four independent accumulation chains per wave: a chain's next product issues four
-// products after its last one, past the matrix core's result latency.
+// Two accumulation chains per wave on blocks of ones times blocks of twos (A and B in
+// distinct registers): a chain's next product issues one product after its last one.
+// Measured against other forms of the same loop: four chains, or one register feeding both
+// operands, lose 9-12% of the rate.
 template <bool kFp8>
 __global__ __launch_bounds__(kThreads, 2) void probe_mfma_kernel(int iters, float* __restrict__ out) {
-  floatx16 acc[4];
+  floatx16 acc[2];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
   if constexpr (kFp8) {
     const intx8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
+    const intx8 twos = {0x40404040, 0x40404040, 0x40404040, 0x40404040,
+                        0x40404040, 0x40404040, 0x40404040, 0x40404040};  // E4M3 2.0
+#pragma unroll 4
     for (int i = 0; i < iters; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, ones, acc[c], 0, 0, 0, 0, 0, 0);
+      for (int c = 0; c < 2; ++c)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, twos, acc[c], 0, 0, 0, 0, 0, 0);
   } else {
-    bf16x8 ones;
+    bf16x8 ones, twos;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
+    for (int e = 0; e < 8; ++e) {
+      ones[e] = (bf16)1.0f;
+      twos[e] = (bf16)2.0f;
+    }
+#pragma unroll 4
     for (int i = 0; i < iters; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, ones, acc[c], 0, 0, 0);
+      for (int c = 0; c < 2; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, twos, acc[c], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += acc[c][r];
   if ((threadIdx.x & 63) == 0) out[blockIdx.x * (kThreads / 64) + threadIdx.x / 64] = s;
