@@ -43,7 +43,15 @@ extern "C" {
 
 #define ATTN_ABI_VERSION 5
 
-typedef enum attn_status {
+/* The enumerations are int-sized.  C++ gets the underlying type spelled out, so that any int
+ * a caller passes (ctypes, C) is a valid value there too and is rejected by the checks. */
+#ifdef __cplusplus
+#define ATTN_INT_ENUM : int
+#else
+#define ATTN_INT_ENUM
+#endif
+
+typedef enum attn_status ATTN_INT_ENUM {
   ATTN_OK = 0,
   ATTN_ERR_INVALID = 1,     /* null pointer, size <= 0, scale not finite or <= 0, bad block size */
   ATTN_ERR_UNSUPPORTED = 2, /* dtype / head_dim / option combination this build has no kernel for */
@@ -51,7 +59,7 @@ typedef enum attn_status {
   ATTN_ERR_LAUNCH = 4       /* the HIP runtime refused the launch (hipGetLastError after it) */
 } attn_status;
 
-typedef enum attn_dtype {
+typedef enum attn_dtype ATTN_INT_ENUM {
   ATTN_F32 = 0,  /* fp32 in, fp32 out */
   ATTN_BF16 = 1  /* bf16 in, bf16 out, fp32 accumulation */
 } attn_dtype;

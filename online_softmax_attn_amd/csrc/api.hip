@@ -2,6 +2,7 @@
 // The contract of every entry point is documented in include/attn.h.
 #include "attn.h"
 
+#include <climits>
 #include <cmath>
 
 #include "common.h"
@@ -10,10 +11,18 @@ namespace {
 
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.f; }
 
-attn_status launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+// a * b * c for factors >= 0, or LLONG_MAX when the product does not fit in 64 bits (the
+// size checks below compare such products against the 32-bit limits of offsets and grids)
+long long mul3(long long a, long long b, long long c) {
+  long long ab = 0, abc = 0;
+  if (__builtin_mul_overflow(a, b, &ab) || __builtin_mul_overflow(ab, c, &abc)) return LLONG_MAX;
+  return abc;
+}
 
-constexpr int kDecodeBlock = 16;
-constexpr int kDecodeMaxSplit = 64 * kDecodeBlock;  // one table entry per lane of a wave
+// number of `tile`-row tiles covering n rows
+long long tiles(int n, int tile) { return ((long long)n + tile - 1) / tile; }
+
+attn_status launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
 // grouped heads and window: heads a positive multiple of kv_heads, window >= 0
 bool heads_window_ok(int heads, int kv_heads, int window) {
@@ -48,6 +57,7 @@ attn_status decode_paged_check(attn_dtype dtype, const void* q, const void* k_ca
   *split = resolve_split(batch, heads, kv_heads, max_seq_len, window, kv_split);
   if (*split == 0) return ATTN_ERR_INVALID;
   *need = decode_workspace_bytes(batch, heads, head_dim, max_seq_len, window, *split);
+  if (*need == 0) return ATTN_ERR_UNSUPPORTED;  // the partials' size does not fit in size_t
   return ATTN_OK;
 }
 
@@ -76,8 +86,8 @@ attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void*
   if (!finite_positive(scale)) return ATTN_ERR_INVALID;
   // 32-bit byte offsets inside one (batch, head) slice
   const long long elem = dtype == ATTN_F32 ? 4 : 2;
-  if ((long long)seq_len * head_dim * elem >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
-  if ((long long)batch * heads * ((seq_len + 127) / 128) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (mul3(seq_len, head_dim, elem) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (mul3(batch, heads, tiles(seq_len, 128)) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ATTN_F32) {
     if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
@@ -108,8 +118,8 @@ attn_status attn_fwd_chunk(attn_dtype dtype, const void* q, const void* k, const
   if (!finite_positive(scale)) return ATTN_ERR_INVALID;
   if (dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   // 32-bit byte offsets inside one (batch, head) slice
-  if ((long long)kv_len * head_dim * 2 >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
-  if ((long long)batch * heads * ((q_len + 127) / 128) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (mul3(kv_len, head_dim, 2) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (mul3(batch, heads, tiles(q_len, 128)) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
   return launch_status(launch_fwd_bf16(static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                                        static_cast<const bf16*>(v), static_cast<bf16*>(o), lse,
                                        nullptr, batch, heads, kv_heads, q_len, kv_len, q_start,
@@ -119,6 +129,7 @@ attn_status attn_fwd_chunk(attn_dtype dtype, const void* q, const void* k, const
 
 size_t attn_bwd_workspace_bytes(int batch, int heads, int seq_len) {
   if (batch <= 0 || heads <= 0 || seq_len <= 0) return 0;
+  if (mul3(batch, heads, tiles(seq_len, 128)) >= (1LL << 31)) return 0;  // attn_bwd rejects it
   return bwd_workspace_bytes(batch, heads, seq_len);
 }
 
@@ -134,8 +145,8 @@ attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void*
   if (!finite_positive(scale)) return ATTN_ERR_INVALID;
   if (dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   // 32-bit byte offsets inside one (batch, head) slice; one fp32 gradient row is 512 bytes
-  if ((long long)seq_len * head_dim * 4 >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
-  if ((long long)batch * heads * ((seq_len + 127) / 128) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (mul3(seq_len, head_dim, 4) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (mul3(batch, heads, tiles(seq_len, 128)) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < bwd_workspace_bytes(batch, heads, seq_len))
     return ATTN_ERR_WORKSPACE;
   return launch_status(launch_bwd_bf16(
@@ -167,9 +178,8 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const 
   if (!finite_positive(scale)) return ATTN_ERR_INVALID;
   if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   // 32-bit byte offsets inside one (batch, head) slice, also of the transposed V
-  const long long n_pad = (seq_len + 63LL) / 64 * 64;
-  if (n_pad * head_dim >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
-  if ((long long)batch * heads * ((seq_len + 127) / 128) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (mul3(tiles(seq_len, 64), 64, head_dim) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (mul3(batch, heads, tiles(seq_len, 128)) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
   return launch_status(launch_fwd_fp8(
       static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
       static_cast<const uint8_t*>(vt8), q_scale, k_scale, v_scale, static_cast<bf16*>(o), lse,
@@ -184,7 +194,7 @@ attn_status attn_merge(attn_dtype dtype, const void* o_parts, const float* lse_p
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (parts > 1024) return ATTN_ERR_UNSUPPORTED;
-  if ((rows + 15) / 16 >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;  // grid: >= 16 rows per workgroup
+  if ((rows - 1) / 16 + 1 >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;  // grid: 16 rows per workgroup
   return launch_status(launch_merge(dtype == ATTN_BF16, o_parts, lse_parts, o, lse, parts,
                                     (long long)rows, head_dim,
                                     reinterpret_cast<hipStream_t>(stream)));
@@ -194,6 +204,7 @@ size_t attn_decode_workspace_bytes(int batch, int heads, int kv_heads, int head_
                                    int max_seq_len, int window, int kv_split) {
   if (batch <= 0 || heads <= 0 || head_dim != 128 || max_seq_len <= 0) return 0;
   if (!heads_window_ok(heads, kv_heads, window)) return 0;
+  if (batch > 65535 || heads > 65535) return 0;  // attn_decode_paged rejects these grids
   const int split = resolve_split(batch, heads, kv_heads, max_seq_len, window, kv_split);
   if (split == 0) return 0;
   return decode_workspace_bytes(batch, heads, head_dim, max_seq_len, window, split);

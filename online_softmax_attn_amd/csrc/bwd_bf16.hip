@@ -562,10 +562,6 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int batch, int heads, int n) {
-  return (size_t)batch * heads * n * sizeof(float);
-}
-
 hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
                            const bf16* dout, const float* lse, const int32_t* seq_lens,
                            float* dq, float* dk, float* dv, int batch, int heads, int kv_heads,

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "attn.h"
+#include "sizing.h"
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -34,7 +35,6 @@ hipError_t launch_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* o,
 
 // Backward pass (bf16 in, fp32 gradients): D = rowsum(dO * O) into `workspace`, then dQ
 // and dK/dV kernels that recompute the weights from the saved log-sum-exp.
-size_t bwd_workspace_bytes(int batch, int heads, int n);
 hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
                            const bf16* dout, const float* lse, const int32_t* seq_lens,
                            float* dq, float* dk, float* dv, int batch, int heads, int kv_heads,
@@ -42,9 +42,6 @@ hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf
                            hipStream_t stream);
 
 // Split-KV paged decode: partials into `workspace`, then the merge pass writes o / lse.
-int decode_default_split(int batch, int heads, int kv_heads, int max_seq_len, int window);
-size_t decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len, int window,
-                              int split);
 hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v_cache,
                                const int32_t* block_table, const int32_t* seq_lens, bf16* o,
                                float* lse, int batch, int heads, int kv_heads, int num_blocks,

@@ -85,7 +85,7 @@ struct Block {
 
 // One wave per (sequence, K/V head, split, group of GQ query heads sharing that K/V head:
 // every block loaded is scored and accumulated GQ times).  Launched with GQ = 1 (plain
-// multi-head attention); groups of kMfmaGroup or more query heads go to decode_gqa_kernel.
+// multi-head attention); groups of kDecodeMfmaGroup or more query heads go to decode_gqa_kernel.
 // Tokens [kbeg, L) are admitted (kbeg > 0 under a window); splits count blocks from the one
 // holding kbeg.
 template <int GQ>
@@ -282,75 +282,16 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   if (lse && lane == 0) lse[(size_t)b * H + h] = mstar * ATTN_LN2 + __logf(lsum);
 }
 
-// Blocks a sequence's admitted tokens can touch: all of them, or under a window of w the
-// w tokens [L - w, L), which straddle at most ceil((w + 15) / 16) blocks.
-int span_blocks(int max_seq_len, int window) {
-  const int all = (max_seq_len + kBlock - 1) / kBlock;
-  return window ? min(all, (window + 2 * kBlock - 2) / kBlock) : all;
-}
-
-int max_splits_for(int max_seq_len, int window, int split) {
-  const int split_blocks = split / kBlock;
-  return (span_blocks(max_seq_len, window) + split_blocks - 1) / split_blocks;
-}
-
-// Groups of at least this many query heads per K/V head run on the matrix cores
-// (decode_gqa_kernel); single heads (plain multi-head attention) on the vector units
-// (decode_split_kernel, one query head per wave).  Measured on 32 sequences of 1024..8192
-// tokens, 8 K/V heads, a 1 GiB write before each call: the matrix-core kernel reads 5.8 /
-// 5.6 / 5.4 / 5.0 TB/s at 2 / 4 / 8 / 16 heads per group, the vector kernel (one wave
-// serving 2 or 4 heads of a group) 5.5 / 4.6 TB/s at 2 / 4.
-constexpr int kMfmaGroup = 2;
-
-// waves per (sequence, split): decode_gqa_kernel takes up to 32 heads of a group per wave
-long long waves_per_split(int heads, int kv_heads) {
-  const int G = heads / kv_heads;
-  if (G >= kMfmaGroup) return (long long)kv_heads * ((G + 31) / 32);
-  return heads;
-}
-
 }  // namespace
-
-// Split length: as long as possible (each split wave streams its blocks back to back) while
-// the grid still offers enough waves to keep every CU's memory pipeline full.  Measured on
-// the decode workload (B=32, H=32, lengths up to 8192): 128 tokens 407 us, 256: 390 us,
-// 512: 376 us, 768: 376 us, 1024: 378 us.
-int decode_default_split(int batch, int heads, int kv_heads, int max_seq_len, int window) {
-  const long long wave_heads = waves_per_split(heads, kv_heads);
-  const long long span = (long long)span_blocks(max_seq_len, window) * kBlock;
-  if (heads / kv_heads >= kMfmaGroup) {
-    // the matrix-core kernel: its waves start with two dependent memory round trips (page
-    // numbers, then the first tiles), so it takes the longest split (at most 1024 tokens)
-    // that still gives 2048 waves.  Measured with 8 K/V heads x 8 query heads, 32 sequences
-    // of 1024..8192 tokens: 128 tokens 4.2 TB/s, 256: 4.6, 512: 4.9, 1024: 5.5.
-    for (int split : {1024, 512, 256, 128}) {
-      const long long waves = (long long)batch * wave_heads * ((span + split - 1) / split);
-      if (waves >= 2048) return split;
-    }
-    return 64;
-  }
-  constexpr long long kTargetWaves = 8192;
-  for (int split : {512, 256, 128}) {
-    const long long waves = (long long)batch * wave_heads * ((span + split - 1) / split);
-    if (waves >= kTargetWaves) return split;
-  }
-  return 64;
-}
-
-size_t decode_workspace_bytes(int batch, int heads, int head_dim, int max_seq_len, int window,
-                              int split) {
-  const size_t n_part = (size_t)batch * heads * max_splits_for(max_seq_len, window, split);
-  return n_part * (2 + (size_t)head_dim) * sizeof(float);
-}
 
 hipError_t launch_decode_paged(const bf16* q, const bf16* k_cache, const bf16* v_cache,
                                const int32_t* block_table, const int32_t* seq_lens, bf16* o,
                                float* lse, int batch, int heads, int kv_heads, int num_blocks,
                                int max_blocks_per_seq, int max_seq_len, int window, float scale,
                                int split, void* workspace, hipStream_t stream) {
-  const int max_splits = max_splits_for(max_seq_len, window, split);
+  const int max_splits = decode_max_splits(max_seq_len, window, split);
   const size_t n_part = (size_t)batch * heads * max_splits;
-  if (heads / kv_heads >= kMfmaGroup) {
+  if (heads / kv_heads >= kDecodeMfmaGroup) {
     const hipError_t e = launch_decode_gqa(q, k_cache, v_cache, block_table, seq_lens, batch, heads,
                                            kv_heads, num_blocks, max_blocks_per_seq, max_seq_len,
                                            window, scale, split, max_splits, workspace, n_part,

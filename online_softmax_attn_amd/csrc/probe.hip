@@ -28,7 +28,6 @@ __global__ __launch_bounds__(kThreads, 2) void probe_mfma_kernel(int iters, floa
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
     const intx8 twos = {0x40404040, 0x40404040, 0x40404040, 0x40404040,
                         0x40404040, 0x40404040, 0x40404040, 0x40404040};  // E4M3 2.0
-#pragma unroll 4
     for (int i = 0; i < iters; ++i)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -40,7 +39,6 @@ __global__ __launch_bounds__(kThreads, 2) void probe_mfma_kernel(int iters, floa
       ones[e] = (bf16)1.0f;
       twos[e] = (bf16)2.0f;
     }
-#pragma unroll 4
     for (int i = 0; i < iters; ++i)
 #pragma unroll
       for (int c = 0; c < 2; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, twos, acc[c], 0, 0, 0);
