@@ -898,18 +898,19 @@ def bench_shapes(args, attn, workloads, torch):
         mk = lambda h: torch.randn(B, h, n, d, generator=g, device=dev).to(dtype)
         return mk(H), mk(Hkv), mk(Hkv)
 
-    for (B, H, Hkv, n, causal) in [(32, 32, 32, 512, True), (16, 32, 32, 1024, True),
-                                   (4, 32, 32, 2048, True), (4, 32, 32, 2048, False),
-                                   (1, 32, 32, 4096, True), (4, 32, 32, 4096, False),
-                                   (2, 32, 32, 8192, True), (1, 32, 32, 16384, True),
-                                   (1, 32, 32, 32768, True), (4, 32, 8, 2048, True),
-                                   (1, 64, 8, 8192, True)]:
-        q, k, v = qkv(B, H, Hkv, n)
+    for (B, H, Hkv, n, d, causal) in [(32, 32, 32, 512, 128, True), (16, 32, 32, 1024, 128, True),
+                                      (4, 32, 32, 2048, 128, True), (4, 32, 32, 2048, 128, False),
+                                      (1, 32, 32, 4096, 128, True), (4, 32, 32, 4096, 128, False),
+                                      (2, 32, 32, 8192, 128, True), (1, 32, 32, 16384, 128, True),
+                                      (1, 32, 32, 32768, 128, True), (4, 32, 8, 2048, 128, True),
+                                      (1, 64, 8, 8192, 128, True), (4, 32, 32, 2048, 64, True),
+                                      (1, 32, 32, 16384, 64, True)]:
+        q, k, v = qkv(B, H, Hkv, n, d)
         o = torch.empty_like(q)
         ms = timed(lambda: attn.attn_fwd(q, k, v, causal=causal, out=o))
         pairs = n * (n + 1) / 2 if causal else n * n
-        emit("prefill bf16", f"[{B},{H},{n},128] kv_heads {Hkv} {'causal' if causal else 'full'}",
-             ms, 4 * 128 * B * H * pairs / ms / 1e9, "TFLOP/s", PEAK_BF16_TFLOPS)
+        emit("prefill bf16", f"[{B},{H},{n},{d}] kv_heads {Hkv} {'causal' if causal else 'full'}",
+             ms, 4 * d * B * H * pairs / ms / 1e9, "TFLOP/s", PEAK_BF16_TFLOPS)
         del q, k, v, o
     for (B, H, n, d, causal, lens) in [(1, 1, 256, 64, False, None),
                                        (4, 4, 1000, 64, True, [1000, 900, 500, 17]),

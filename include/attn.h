@@ -85,7 +85,7 @@ typedef enum attn_dtype ATTN_INT_ENUM {
  * Errors     : ATTN_ERR_INVALID also for kv_heads <= 0, heads % kv_heads != 0, window < 0
  *              or a window without causal.
  * Supported  : ATTN_F32 with head_dim 64 or 128 (scores accumulated in fp64);
- *              ATTN_BF16 with head_dim 128 (MFMA, fp32 accumulation).
+ *              ATTN_BF16 with head_dim 128 or 64 (MFMA, fp32 accumulation).
  */
 attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void* v, void* o,
                      float* lse, const int32_t* seq_lens, int batch, int heads, int kv_heads,
@@ -102,15 +102,16 @@ attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void*
  * prefill chunk against a cached prefix; each query block is independent work, as in the
  * query-outer loop of pierluigilucio.it ("I Due Pilastri di FlashAttention", FA2).
  *
- * q, o       : [batch, heads, q_len, 128] bf16, contiguous; o written in full.
- * k, v       : [batch, kv_heads, kv_len, 128] bf16, contiguous.
+ * q, o       : [batch, heads, q_len, head_dim] bf16, contiguous; o written in full.
+ * k, v       : [batch, kv_heads, kv_len, head_dim] bf16, contiguous (head_dim 128 or 64).
  * lse        : optional fp32 [batch, heads, q_len], as in attn_fwd.
  * causal     : nonzero => query row i admits keys j <= q_start + i.
  * window     : 0, or w > 0 with causal: row i admits keys q_start + i - w < j <= q_start + i.
  * Errors     : ATTN_ERR_INVALID for null q/k/v/o, sizes <= 0, q_start < 0,
  *              q_start + q_len > kv_len, kv_heads <= 0 or not dividing heads, window < 0 or
  *              without causal, scale not finite or <= 0; ATTN_ERR_UNSUPPORTED for a dtype
- *              other than ATTN_BF16, head_dim != 128, or sizes past the 32-bit offsets.
+ *              other than ATTN_BF16, head_dim not 128 or 64, or sizes past the 32-bit
+ *              offsets.
  * With q_start = 0 and q_len = kv_len it computes what attn_fwd computes (no seq_lens).
  */
 attn_status attn_fwd_chunk(attn_dtype dtype, const void* q, const void* k, const void* v,

@@ -173,8 +173,8 @@ def _kv_heads(q, k, v):
 @_on_stream
 def attn_fwd(q, k, v, *, causal=False, window=0, scale=None, seq_lens=None, out=None,
              lse=None, return_lse=False, stream=None):
-    """Prefill attention: q [B, H, n, d], k and v [B, H_kv, n, d] (fp32 d in {64,128};
-    bf16 d = 128).
+    """Prefill attention: q [B, H, n, d], k and v [B, H_kv, n, d] (d in {64, 128}, fp32 or
+    bf16).
 
     seq_lens: optional per-batch lengths (host sequence or device int32 tensor); rows past
     a length are padding (output 0, lse -inf).  window > 0 (with causal) limits query i to
@@ -213,7 +213,7 @@ def attn_fwd(q, k, v, *, causal=False, window=0, scale=None, seq_lens=None, out=
 @_on_stream
 def attn_fwd_chunk(q, k, v, q_start, *, causal=False, window=0, scale=None, out=None,
                    lse=None, return_lse=False, stream=None):
-    """A chunk of queries against a longer key sequence (bf16, d = 128): q [B, H, n_q, d] are
+    """A chunk of queries against a longer key sequence (bf16, d in {64, 128}): q [B, H, n_q, d] are
     positions q_start .. q_start + n_q - 1 of the sequence whose keys and values are
     k, v [B, H_kv, n_kv, d]; the causal mask and the window count those positions.
     Returns o, or (o, lse) with return_lse."""

@@ -98,11 +98,11 @@ attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void*
                                         causal != 0, window, scale, s));
   }
   if (dtype == ATTN_BF16) {
-    if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    if (head_dim != 128 && head_dim != 64) return ATTN_ERR_UNSUPPORTED;
     return launch_status(launch_fwd_bf16(static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                                          static_cast<const bf16*>(v), static_cast<bf16*>(o), lse,
                                          seq_lens, batch, heads, kv_heads, seq_len, seq_len, 0,
-                                         causal != 0, window, scale, s));
+                                         head_dim, causal != 0, window, scale, s));
   }
   return ATTN_ERR_UNSUPPORTED;
 }
@@ -116,14 +116,14 @@ attn_status attn_fwd_chunk(attn_dtype dtype, const void* q, const void* k, const
   if (q_start < 0 || (long long)q_start + q_len > kv_len) return ATTN_ERR_INVALID;
   if (!heads_window_ok(heads, kv_heads, window) || (window > 0 && !causal)) return ATTN_ERR_INVALID;
   if (!finite_positive(scale)) return ATTN_ERR_INVALID;
-  if (dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16 || (head_dim != 128 && head_dim != 64)) return ATTN_ERR_UNSUPPORTED;
   // 32-bit byte offsets inside one (batch, head) slice
   if (mul3(kv_len, head_dim, 2) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
   if (mul3(batch, heads, tiles(q_len, 128)) >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;
   return launch_status(launch_fwd_bf16(static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                                        static_cast<const bf16*>(v), static_cast<bf16*>(o), lse,
                                        nullptr, batch, heads, kv_heads, q_len, kv_len, q_start,
-                                       causal != 0, window, scale,
+                                       head_dim, causal != 0, window, scale,
                                        reinterpret_cast<hipStream_t>(stream)));
 }
 

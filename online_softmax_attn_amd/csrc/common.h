@@ -27,11 +27,12 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           int head_dim, int causal, int window, float scale, hipStream_t stream);
 
 // bf16 prefill: n query rows at positions q_start .. q_start + n - 1 of a key sequence of
-// n_kv rows (the plain call: n_kv = n, q_start = 0; seq_lens only with the plain call).
+// n_kv rows (the plain call: n_kv = n, q_start = 0; seq_lens only with the plain call);
+// head_dim 128 or 64.
 hipError_t launch_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* lse,
                            const int32_t* seq_lens, int batch, int heads, int kv_heads, int n,
-                           int n_kv, int q_start, int causal, int window, float scale,
-                           hipStream_t stream);
+                           int n_kv, int q_start, int head_dim, int causal, int window,
+                           float scale, hipStream_t stream);
 
 // Backward pass (bf16 in, fp32 gradients): D = rowsum(dO * O) into `workspace`, then dQ
 // and dK/dV kernels that recompute the weights from the saved log-sum-exp.

@@ -1,4 +1,4 @@
-// bf16 prefill attention on gfx950 matrix cores, head_dim 128.
+// bf16 prefill attention on gfx950 matrix cores, head_dim 128 (and 64).
 //
 // Method: the score matrix is produced and consumed one 64-key tile at a time with the
 // running (m, l, u) summary of el-ai.com "Attenzione: softmax online, riscalamento e
@@ -18,7 +18,7 @@
 //     bf16 weights P^T feed the MFMA B operand straight from the score registers; V^T is
 //     read from a row-major V tile with ds_read_b64_tr_b16, whose 16-lane transpose hands
 //     each lane 4 consecutive keys of one dimension.
-//   * K/V tiles (64 x 128 bf16 = 16 KiB each) are double-buffered in LDS and filled by
+//   * K/V tiles (64 x 128 bf16 = 16 KiB each; 8 KiB at head_dim 64) are double-buffered in LDS and filled by
 //     16-byte-per-lane buffer loads that write LDS directly (no register staging), each lane
 //     fetching the chunk an XOR swizzle puts in its slot; the swizzle keeps both the K row
 //     reads and the transposed V reads free of bank conflicts.  K runs two tiles ahead of
@@ -43,24 +43,31 @@
 
 namespace {
 
-constexpr int kD = 128;      // head dim
 constexpr int kBM = 128;     // queries per workgroup
 constexpr int kBN = 64;      // keys per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTileElems = kBN * kD;
 constexpr float kSlack = 8.0f;  // log2 headroom of the lazily raised reference maximum
 
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-// LDS element offset of logical 16-byte chunk `c` (0..15) of row `r` in a K tile: the chunk
-// index is XORed with r % 16, so the 16 rows one MFMA operand read touches hit 16 distinct
-// chunk slots.
-__device__ __forceinline__ int k_slot(int r, int c) { return r * kD + ((c ^ (r & 15)) << 3); }
-// Same for a V tile: chunk groups of 64 bytes are XORed with r % 4, so the 8 rows one
-// transposed read touches spread over all four 64-byte bank groups.
-__device__ __forceinline__ int v_slot(int r, int c) { return r * kD + ((c ^ ((r & 3) << 2)) << 3); }
+// Tile swizzles, per head dim D (rows of D bf16, 16-byte chunks c = 0 .. D/8 - 1).
+// D = 128 (256-byte rows, one row spans all LDS banks): a K row's chunk index is XORed with
+// r % 16, so the 16 rows one MFMA operand read touches hit 16 distinct chunk slots; in a V
+// tile, chunk groups of 64 bytes are XORed with r % 4, so the 8 rows one transposed read
+// touches spread over all four 64-byte bank groups.
+// D = 64 (128-byte rows, even and odd rows in the two halves of the banks): K chunks are
+// XORed with (r / 2) % 8, which again separates 16 consecutive rows; V chunk groups with
+// (r / 2) % 2, which halves the conflicts of a transposed read (two 64-byte groups per row).
+template <int D>
+__device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swz(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+template <int D>
+__device__ __forceinline__ int k_slot(int r, int c) { return r * D + ((c ^ k_swz<D>(r)) << 3); }
+template <int D>
+__device__ __forceinline__ int v_slot(int r, int c) { return r * D + ((c ^ v_swz<D>(r)) << 3); }
 
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
@@ -90,8 +97,9 @@ struct Tile {
 };
 
 // kWindow: a causal window is in force (`window` > 0); without it the window terms compile
-// away and the register budget of the plain kernel is untouched.
-template <bool kWindow>
+// away and the register budget of the plain kernel is untouched.  kD: the head dim, 128 or
+// 64 (half the Q operand, accumulator, tile and products per step; the same steps).
+template <bool kWindow, int kD>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ lens, int B,
@@ -100,6 +108,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // Q, O, LSE hold n query rows; K, V hold n_kv key rows.  Query row r sits at position
   // q_start + r of the key sequence (the causal mask and the window count positions); the
   // plain call has n_kv = n and q_start = 0.  Lengths (lens) apply to plain calls only.
+  constexpr int kTileElems = kBN * kD;
+  constexpr int kChunks = kD / 8;        // 16-byte chunks per row
+  constexpr int kKSteps = kD / 16;       // k-steps of a score product (Q^T operand registers)
+  constexpr int kDBlocks = kD / 32;      // 32-wide output blocks (accumulators)
+  constexpr int kSlices = kD / 32;       // 1 KiB slices of a tile each wave fills
+  constexpr int kSliceRows = 512 / kD;   // tile rows per 1 KiB slice
   // K tiles in slots 0 and 1, V tiles in slots 2 and 3 (one LDS object: the compiler then
   // keeps the non-aliasing of the four slots declared below)
   __shared__ __attribute__((aligned(1024))) bf16 tiles[4][kTileElems];
@@ -143,10 +157,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // rows >= L read as zeros through the descriptors' range
   const rsrc_t rq = make_rsrc(Q + base, (uint32_t)(min(L - q_start, n)) * kD * 2);
 
-  // Q^T operand: lane (query lq, half hl) holds dims 16*ks + 8*hl .. +7 for ks = 0..7.
-  bf16x8 qop[8];
+  // Q^T operand: lane (query lq, half hl) holds dims 16*ks + 8*hl .. +7 for ks < kD/16.
+  bf16x8 qop[kKSteps];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
+  for (int ks = 0; ks < kKSteps; ++ks)
     qop[ks] = load_b128(rq, ((qi - q_start) * kD + 16 * ks + 8 * hl) * 2);
 
   const int kend = causal ? min(L, p0 + kBM) : L;
@@ -157,18 +171,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // tiles a wave takes part in (causal: none strictly above its diagonal)
   const int wave_tiles = causal ? min(n_tiles, wave_q_last / kBN + 1) : n_tiles;
 
-  // Direct global->LDS tile fill: wave w fills 1 KiB slices 4w..4w+3 of each tile; lane i of
-  // slice j lands in row 4j + i/16, physical chunk i%16, so it fetches the logical chunk the
-  // swizzle puts there.  Each tile is read through a descriptor whose base is the tile's
-  // first row and whose range ends at row L, so the per-lane offsets are loop invariants
-  // and rows past L still read as zeros.
-  int k_src[4], v_src[4];
+  // Direct global->LDS tile fill: wave w fills 1 KiB slices kSlices*w .. +kSlices-1 of each
+  // tile; lane i of slice j lands in row kSliceRows*j + i/kChunks, physical chunk
+  // i%kChunks, so it fetches the logical chunk the swizzle puts there.  Each tile is read
+  // through a descriptor whose base is the tile's first row and whose range ends at row L,
+  // so the per-lane offsets are loop invariants and rows past L still read as zeros.
+  int k_src[kSlices], v_src[kSlices];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * (4 * w + i) + (lane >> 4);
-    const int pc = lane & 15;
-    k_src[i] = (r * kD + 8 * (pc ^ (r & 15))) * 2;
-    v_src[i] = (r * kD + 8 * (pc ^ ((r & 3) << 2))) * 2;
+  for (int i = 0; i < kSlices; ++i) {
+    const int r = kSliceRows * (kSlices * w + i) + lane / kChunks;
+    const int pc = lane % kChunks;
+    k_src[i] = (r * kD + 8 * (pc ^ k_swz<kD>(r))) * 2;
+    v_src[i] = (r * kD + 8 * (pc ^ v_swz<kD>(r))) * 2;
   }
   const bf16* k_head = K + kv_base;
   const bf16* v_head = V + kv_base;
@@ -176,25 +190,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int first = t * kBN;
     return make_rsrc(head + (size_t)first * kD, (uint32_t)max(L - first, 0) * kD * 2);
   };
-  // this wave's 4 KiB slice of a tile, as a wave-uniform (scalar) LDS byte offset
-  const int lds_w = __builtin_amdgcn_readfirstlane(w * 4 * 512 * 2);
+  // this wave's slices of a tile, as a wave-uniform (scalar) LDS byte offset
+  const int lds_w = __builtin_amdgcn_readfirstlane(w * kSlices * 1024);
   auto lds_dst = [&](bf16* tile, int i) __attribute__((always_inline)) {
     return (lds_void*)((lds_char*)(lds_void*)tile + lds_w + i * 1024);
   };
   auto issue_k = [&](int t, bf16* Kd) __attribute__((always_inline)) {
     const rsrc_t r = tile_rsrc(k_head, t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_lds16(r, lds_dst(Kd, i), k_src[i]);
+    for (int i = 0; i < kSlices; ++i) load_lds16(r, lds_dst(Kd, i), k_src[i]);
   };
   auto issue_v = [&](int t, bf16* Vd) __attribute__((always_inline)) {
     const rsrc_t r = tile_rsrc(v_head, t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_lds16(r, lds_dst(Vd, i), v_src[i]);
+    for (int i = 0; i < kSlices; ++i) load_lds16(r, lds_dst(Vd, i), v_src[i]);
   };
 
-  floatx16 acc[4];  // O^T, d blocks of 32: lane holds d = 32*db + 8*(r/4) + 4*hl + r%4
+  floatx16 acc[kDBlocks];  // O^T, d blocks of 32: lane holds d = 32*db + 8*(r/4) + 4*hl + r%4
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   // Reference maximum (log2 units) the weights are taken against.  It follows the running
@@ -218,17 +232,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int tr_col = 16 * (g & 1) + 4 * (s & 3);           // + 32*db
 
   // ---- building blocks ----------------------------------------------------------------
-  auto compute_s = [&](Tile& T, const bf16* Kt) __attribute__((always_inline)) {  // S^T = K Q^T, 16 MFMA + 16 LDS reads
+  auto compute_s = [&](Tile& T, const bf16* Kt) __attribute__((always_inline)) {  // S^T = K Q^T, 2 kD/16 MFMA + LDS reads
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) T.s[kb][r] = 0.f;
     }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < kKSteps; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&Kt[k_slot(32 * kb + lq, 2 * ks + hl)]);
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&Kt[k_slot<kD>(32 * kb + lq, 2 * ks + hl)]);
         T.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], T.s[kb], 0, 0, 0);
       }
   };
@@ -279,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
     }
@@ -315,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       m_use = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       psum = weights(T, pop);
@@ -326,13 +340,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < kDBlocks; ++db) {
         const int col = 32 * db + tr_col;
         const int r_lo = 16 * grp + tr_row;
         const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_shortx4*)(&Vt[v_slot(r_lo, col >> 3) + (col & 7)]));
+            (lds_shortx4*)(&Vt[v_slot<kD>(r_lo, col >> 3) + (col & 7)]));
         const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_shortx4*)(&Vt[v_slot(r_lo + 8, col >> 3) + (col & 7)]));
+            (lds_shortx4*)(&Vt[v_slot<kD>(r_lo + 8, col >> 3) + (col & 7)]));
         const bf16x8 vop = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
                                                    __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3,
                                                    4, 5, 6, 7);
@@ -361,21 +375,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     __builtin_amdgcn_s_setprio(1);
     compute_s(nxt, Kr);
     const float psum = weights(cur, pop);
-    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+    // kS score products (one operand read each), ~96 VALU instructions of weights
+    constexpr int kS = 2 * kKSteps;
+    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, kS / 4, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kS; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedVALU, 6, 0);
-      if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVALU, 96 / kS, 0);
+      if (i < kS - kS / 4) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
     }
     checked_weights(cur, pop, psum);
     __builtin_amdgcn_s_setprio(0);
     pv(Vr, pop);
-    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 8, 1);
+    // kP P.V products (two transposed reads each)
+    constexpr int kP = 4 * kDBlocks;
+    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, kP / 2, 1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kP; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 1);
-      if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 1);
+      if (i < kP - kP / 4) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 1);
     }
     // tile t+1 is used unless it is the last tile and lies past this wave's diagonal
     if ((t + 1 < wave_tiles || t + 1 < t_last) && need_mask(t + 1)) apply_mask(nxt, (t + 1) * kBN);
@@ -406,11 +424,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     issue_k(t0, k0);
     issue_v(t0, v0);
     if (t0 + 1 < n_tiles) issue_k(t0 + 1, k1);
-    // Q and K(t0) have landed once at most the later fills (4 instructions each) are in flight
+    // Q and K(t0) have landed once at most the later fills (kSlices instructions each) are
+    // in flight
     if (t0 + 1 < n_tiles)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kSlices));
     else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kSlices));
     // a bare barrier: __syncthreads() would also wait for the fills still in flight
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -440,29 +459,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   asm volatile("s_mov_b32 %0, 0" : "=s"(hidden_zero));
   sweep(tiles[0] + hidden_zero, tiles[1] + hidden_zero, tiles[2] + hidden_zero, tiles[3] + hidden_zero);
 
-  // ---- epilogue: o = u / l, staged through LDS so that each store instruction writes four
-  // whole 256-byte rows of O.  Every wave has passed the last step's barrier, so the K
-  // buffers are free: wave w takes 8 KiB of them, its 32 rows with the 16-byte chunks of row
-  // r XOR-swizzled by r % 16.
+  // ---- epilogue: o = u / l, staged through LDS so that each store instruction writes whole
+  // rows of O (four of 256 bytes, or eight of 128 at head_dim 64).  Every wave has passed
+  // the last step's barrier, so the K buffers are free: wave w takes 32 rows of them, the
+  // 16-byte chunks of row r XOR-swizzled by r % (chunks per row).
   const float l_tot = other_half_sum(l_run);
   const bool valid = qi < L;
   const float inv = 1.0f / l_tot;
   bf16* stage = &tiles[0][0] + w * (32 * kD);
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       floatx4 x;
 #pragma unroll
       for (int c = 0; c < 4; ++c) x[c] = valid ? acc[db][4 * a + c] * inv : 0.f;
-      const int chunk = (4 * db + a) ^ (lq & 15);
+      const int chunk = (4 * db + a) ^ (lq & (kChunks - 1));
       *reinterpret_cast<bf16x4*>(stage + lq * kD + 8 * chunk + 4 * hl) =
           __builtin_convertvector(x, bf16x4);
     }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 4 * j + (lane >> 4), c = lane & 15;
-    const bf16x8 y = *reinterpret_cast<const bf16x8*>(stage + r * kD + 8 * (c ^ (r & 15)));
+  for (int j = 0; j < kChunks / 2; ++j) {
+    const int r = (64 / kChunks) * j + lane / kChunks, c = lane % kChunks;
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(stage + r * kD + 8 * (c ^ (r & (kChunks - 1))));
     const int row = m0 + w * 32 + r;
     if (row < n) *reinterpret_cast<bf16x8*>(O + base + (size_t)row * kD + 8 * c) = y;
   }
@@ -474,17 +493,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
 hipError_t launch_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* lse,
                            const int32_t* seq_lens, int batch, int heads, int kv_heads, int n,
-                           int n_kv, int q_start, int causal, int window, float scale,
-                           hipStream_t stream) {
+                           int n_kv, int q_start, int head_dim, int causal, int window,
+                           float scale, hipStream_t stream) {
   const int n_qtiles = (n + kBM - 1) / kBM;
   const dim3 grid((unsigned)n_qtiles * batch * heads);
-  if (window > 0)
-    hipLaunchKernelGGL(fwd_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, q, k, v, o, lse,
-                       seq_lens, batch, heads, kv_heads, n, n_kv, q_start, n_qtiles, causal,
-                       window, scale * ATTN_LOG2E);
-  else
-    hipLaunchKernelGGL(fwd_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, q, k, v, o, lse,
-                       seq_lens, batch, heads, kv_heads, n, n_kv, q_start, n_qtiles, causal, 0,
-                       scale * ATTN_LOG2E);
+  const float c = scale * ATTN_LOG2E;
+  const int w = window > 0 ? window : 0;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, q, k, v, o, lse, seq_lens, batch,
+                       heads, kv_heads, n, n_kv, q_start, n_qtiles, causal, w, c);
+  };
+  if (head_dim == 64) {
+    if (w > 0) go(fwd_bf16_kernel<true, 64>);
+    else go(fwd_bf16_kernel<false, 64>);
+  } else {
+    if (w > 0) go(fwd_bf16_kernel<true, 128>);
+    else go(fwd_bf16_kernel<false, 128>);
+  }
   return hipGetLastError();
 }

@@ -17,11 +17,12 @@ hipError_t launch_fwd_f32(const float*, const float*, const float*, float*, floa
   return reached("fwd_f32");
 }
 hipError_t launch_fwd_bf16(const bf16*, const bf16*, const bf16*, bf16*, float*, const int32_t*,
-                           int, int, int, int n, int n_kv, int q_start, int, int, float,
-                           hipStream_t) {
+                           int, int, int, int n, int n_kv, int q_start, int head_dim, int, int,
+                           float, hipStream_t) {
   g_log.n = n;
   g_log.n_kv = n_kv;
   g_log.q_start = q_start;
+  g_log.head_dim = head_dim;
   return reached("fwd_bf16");
 }
 hipError_t launch_bwd_bf16(const bf16*, const bf16*, const bf16*, const bf16*, const bf16*,

@@ -66,7 +66,7 @@ attn_status fwd(Fwd a) {
 void check_fwd() {
   Fwd a;
   ACCEPT(fwd(a), "fwd_bf16");
-  EXPECT(g_log.n == 16 && g_log.n_kv == 16 && g_log.q_start == 0);
+  EXPECT(g_log.n == 16 && g_log.n_kv == 16 && g_log.q_start == 0 && g_log.head_dim == 128);
   Fwd f32;
   f32.dtype = ATTN_F32;
   f32.d = 64;
@@ -111,7 +111,11 @@ void check_fwd() {
   REJECT(fwd(dt), ATTN_ERR_UNSUPPORTED);
   Fwd b64;
   b64.d = 64;
-  REJECT(fwd(b64), ATTN_ERR_UNSUPPORTED);
+  ACCEPT(fwd(b64), "fwd_bf16");
+  EXPECT(g_log.head_dim == 64);
+  Fwd b32;
+  b32.d = 32;
+  REJECT(fwd(b32), ATTN_ERR_UNSUPPORTED);
   // extremes: every size product must be formed without overflow
   Fwd e1;
   e1.n = INT_MAX;

@@ -92,7 +92,7 @@ def fwd(**kw):
     (dict(o=None), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(n=0), INVALID),
     (dict(d=0), INVALID), (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
-    (dict(d=64), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(dtype=0, d=96), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(dtype=0, d=96), UNSUPPORTED),
     (dict(dtype=7), UNSUPPORTED), (dict(n=1 << 24, d=128), UNSUPPORTED),
     (dict(Hkv=0), INVALID), (dict(H=4, Hkv=3), INVALID), (dict(H=4, Hkv=8), INVALID),
     (dict(window=-1, causal=1), INVALID), (dict(window=8, causal=0), INVALID),
@@ -242,7 +242,7 @@ def ch(**kw):
     (dict(q0=201), INVALID), (dict(nq=301, q0=0), INVALID), (dict(Hkv=0), INVALID),
     (dict(H=4, Hkv=3), INVALID), (dict(window=-1), INVALID), (dict(window=8, causal=0), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
-    (dict(dt=attn.ATTN_F32), UNSUPPORTED), (dict(dt=7), UNSUPPORTED), (dict(d=64), UNSUPPORTED),
+    (dict(dt=attn.ATTN_F32), UNSUPPORTED), (dict(dt=7), UNSUPPORTED), (dict(d=32), UNSUPPORTED),
     (dict(nkv=1 << 24, nq=16, q0=0), UNSUPPORTED),
 ])
 def test_fwd_chunk_validation(kw, status):

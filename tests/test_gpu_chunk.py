@@ -37,12 +37,21 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("B,H,Hkv,nq,nkv,q0,causal,window", CASES)
-def test_chunk_matches_oracle(B, H, Hkv, nq, nkv, q0, causal, window):
-    print(f"case: chunk B={B} H={H} Hkv={Hkv} n_q={nq} n_kv={nkv} q_start={q0} causal={causal} window={window}",
+# head_dim 64 (the same kernel at half the dims)
+D64_CASES = [
+    (2, 4, 2, 100, 300, 200, True, 0),
+    (1, 4, 2, 200, 900, 650, True, 128),
+    (2, 2, 1, 257, 700, 300, False, 0),
+]
+
+
+@pytest.mark.parametrize("d,B,H,Hkv,nq,nkv,q0,causal,window",
+                         [(128, *c) for c in CASES] + [(64, *c) for c in D64_CASES])
+def test_chunk_matches_oracle(d, B, H, Hkv, nq, nkv, q0, causal, window):
+    print(f"case: chunk d={d} B={B} H={H} Hkv={Hkv} n_q={nq} n_kv={nkv} q_start={q0} causal={causal} window={window}",
           flush=True)
-    q, _, _ = workloads.prefill(B, H, nq, 128, seed=nq + nkv + q0, kv_heads=Hkv)
-    _, k, v = workloads.prefill(B, H, nkv, 128, seed=7 * nkv + q0, kv_heads=Hkv)
+    q, _, _ = workloads.prefill(B, H, nq, d, seed=nq + nkv + q0, kv_heads=Hkv)
+    _, k, v = workloads.prefill(B, H, nkv, d, seed=7 * nkv + q0, kv_heads=Hkv)
     o, lse = attn.attn_fwd_chunk(q.cuda(), k.cuda(), v.cuda(), q0, causal=causal, window=window,
                                  return_lse=True)
     torch.cuda.synchronize()
@@ -53,9 +62,9 @@ def test_chunk_matches_oracle(B, H, Hkv, nq, nkv, q0, causal, window):
     np.testing.assert_allclose(lse, rl, rtol=0, atol=BF16_LSE_ATOL)
 
 
-@pytest.mark.parametrize("window", [0, 300])
-def test_aligned_chunks_reproduce_the_whole_sequence_bit_for_bit(window):
-    q, k, v = (x.cuda() for x in workloads.prefill(2, 4, 1000, 128, seed=91, kv_heads=2))
+@pytest.mark.parametrize("d,window", [(128, 0), (128, 300), (64, 0), (64, 300)])
+def test_aligned_chunks_reproduce_the_whole_sequence_bit_for_bit(d, window):
+    q, k, v = (x.cuda() for x in workloads.prefill(2, 4, 1000, d, seed=91, kv_heads=2))
     whole, whole_l = attn.attn_fwd(q, k, v, causal=True, window=window, return_lse=True)
     cuts = [0, 128, 512, 640, 1000]
     for a, c in zip(cuts[:-1], cuts[1:]):

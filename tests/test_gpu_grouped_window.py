@@ -63,11 +63,22 @@ BF16_CASES = [
 ]
 
 
-@pytest.mark.parametrize("B,H,Hkv,n,causal,window,lens", BF16_CASES)
-def test_bf16_grouped_window(B, H, Hkv, n, causal, window, lens):
-    q, k, v = workloads.prefill(B, H, n, 128, seed=13 * n + H + window, lens=lens,
+# the same at head_dim 64
+BF16_D64_CASES = [
+    (1, 4, 1, 300, True, 0, None),
+    (2, 8, 2, 257, True, 64, [257, 100]),
+    (1, 4, 2, 700, True, 200, None),
+    (1, 4, 4, 1000, True, 1, None),
+    (2, 32, 8, 300, True, 100, [300, 150]),
+]
+
+
+@pytest.mark.parametrize("d,B,H,Hkv,n,causal,window,lens",
+                         [(128, *c) for c in BF16_CASES] + [(64, *c) for c in BF16_D64_CASES])
+def test_bf16_grouped_window(d, B, H, Hkv, n, causal, window, lens):
+    q, k, v = workloads.prefill(B, H, n, d, seed=13 * n + H + window, lens=lens,
                                 poison=lens is not None, kv_heads=Hkv)
-    print(f"case: bf16 B={B} H={H} Hkv={Hkv} n={n} causal={causal} window={window} lens={lens}",
+    print(f"case: bf16 d={d} B={B} H={H} Hkv={Hkv} n={n} causal={causal} window={window} lens={lens}",
           flush=True)
     o, lse = gpu_fwd(q, k, v, causal=causal, window=window, seq_lens=lens)
     ro, rl = oracle.attention(q, k, v, causal=causal, window=window, seq_lens=lens)

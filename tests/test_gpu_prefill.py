@@ -135,6 +135,35 @@ def test_bf16_more_tiles_than_resident_workgroups(B, H, n, causal, lens):
     np.testing.assert_allclose(lse[rows], rl[rows], rtol=0, atol=BF16_LSE_ATOL)
 
 
+# head_dim 64: the same kernel instantiated for half the dims (half the operand registers,
+# accumulators, tile bytes and products per step); the same bf16 bar
+BF16_D64_CASES = [
+    (1, 1, 1, False, None), (1, 2, 17, True, None), (2, 2, 129, True, None),
+    (2, 2, 300, False, [300, 77]), (3, 2, 200, True, [1, 150, 200]), (1, 4, 1000, True, None),
+    (2, 32, 300, True, [300, 77]), (4, 16, 2048, True, [2048, 1000, 300, 17]),
+]
+
+
+@pytest.mark.parametrize("B,H,n,causal,lens", BF16_D64_CASES)
+def test_bf16_head_dim_64(B, H, n, causal, lens):
+    q, k, v = workloads.prefill(B, H, n, 64, seed=5 * n + B + H, lens=lens, poison=lens is not None)
+    print(f"case: bf16 d=64 B={B} H={H} n={n} causal={causal} lens={lens}", flush=True)
+    o, lse = gpu_fwd(q, k, v, causal=causal, seq_lens=lens)
+    ro, rl = oracle.attention(q, k, v, causal=causal, seq_lens=lens)
+    rows = valid_rows(B, H, n, lens)
+    mx, mean = errs(o, ro, rows)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    check_padding(o, lse, lens)
+    np.testing.assert_allclose(lse[rows], rl[rows], rtol=0, atol=BF16_LSE_ATOL)
+
+
+def test_bf16_head_dim_64_deterministic():
+    q, k, v = workloads.prefill(2, 4, 777, 64, seed=43)
+    a, _ = gpu_fwd(q, k, v, causal=True)
+    b, _ = gpu_fwd(q, k, v, causal=True)
+    assert np.array_equal(a, b)
+
+
 def test_bf16_causal_prefill_workload():
     w = workloads.causal_prefill()
     print("case: causal prefill bf16 [4,32,2048,128]", flush=True)
