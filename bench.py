@@ -56,6 +56,9 @@ host cores this process may run on, and the GPU clock sampled during the timed s
             4 KiB pages in random order, each with its checksum verified.
 --profile-pass    one 1 GiB device copy, one causal prefill and one decode, then exit (the
                   command the rocprofv3 counter runs wrap).
+--profile-pass long
+                  30 long-context prefills back to back, then exit (counters of the long
+                  prefill under sustained load).
 --record-traffic FETCH_CSV WRITE_CSV
                   reads the counter_collection.csv of a FETCH_SIZE and of a WRITE_SIZE run
                   of --profile-pass, scales each counter by what it read for the 1 GiB
@@ -145,15 +148,15 @@ def host_cores():
 
 # --------------------------------------------------------------------------- timing helpers
 class ClockSampler:
-    """GPU shader-clock readings (MHz) polled every ~5 ms on a side thread while phases run;
-    `mark(name)` labels what runs from then on.  The source is the SMI library's GPU
-    metrics table (mean of the per-XCD current GFX clocks), read through the handle torch
-    keeps for it.  The firmware refreshes that table about once per second, so only the
-    readings with a new firmware timestamp are kept: each is the clock at one refresh, and
-    a phase shorter than a second may hold none."""
+    """GPU shader-clock (MHz) and socket-power (W) readings polled every ~5 ms on a side
+    thread while phases run; `mark(name)` labels what runs from then on.  The source is the
+    SMI library's GPU metrics table (mean of the per-XCD current GFX clocks, current socket
+    power), read through the handle torch keeps for it.  The firmware refreshes that table
+    about once per second, so only the readings with a new firmware timestamp are kept:
+    each is the state at one refresh, and a phase shorter than a second may hold none."""
 
     def __init__(self):
-        self.samples = []          # (phase, t, MHz)
+        self.samples = []          # (phase, t, MHz, W)
         self.phase = "idle"
         self.error = None
         self._stop = threading.Event()
@@ -169,11 +172,13 @@ class ClockSampler:
         def read():
             m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
             ts = m.get("firmware_timestamp")
-            xs = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and x > 0]
+            w = m.get("current_socket_power")
+            w = float(w) if isinstance(w, (int, float)) else 0.0
+            xs = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 10000]
             if xs:
-                return sum(xs) / len(xs), ts
+                return sum(xs) / len(xs), w, ts
             x = m.get("current_gfxclk")
-            return (float(x) if isinstance(x, (int, float)) else 0.0), ts
+            return (float(x) if isinstance(x, (int, float)) else 0.0), w, ts
 
         read()
         return read
@@ -190,13 +195,13 @@ class ClockSampler:
             last = None
             while not self._stop.is_set():
                 try:
-                    mhz, ts = self._read()
+                    mhz, watts, ts = self._read()
                 except Exception as e:
                     self.error = f"{type(e).__name__}: {e}"[:200]
                     return
                 if ts != last:  # a refresh of the table
                     last = ts
-                    self.samples.append((self.phase, time.perf_counter() - t0, float(mhz)))
+                    self.samples.append((self.phase, time.perf_counter() - t0, float(mhz), watts))
                 self._stop.wait(0.005)
 
         self._t = threading.Thread(target=run, daemon=True)
@@ -212,13 +217,18 @@ class ClockSampler:
             self._t.join(timeout=2)
 
     def summary(self, phases):
-        vals = [m for p, _, m in self.samples if p in phases and m > 0]
-        out = {"source": "amdsmi GPU metrics, mean of the per-XCD current GFX clocks, one "
-                         "reading per refresh of the table (about once per second)",
+        vals = [m for p, _, m, _ in self.samples if p in phases and m > 0]
+        watts = [w for p, _, m, w in self.samples if p in phases and m > 0 and w > 0]
+        out = {"source": "amdsmi GPU metrics, mean of the per-XCD current GFX clocks and the "
+                         "current socket power, one reading per refresh of the table (about "
+                         "once per second)",
                "phases": sorted(phases), "readings": len(vals)}
         if vals:
             out.update(median_mhz=round(statistics.median(vals), 1), min_mhz=round(min(vals), 1),
                        max_mhz=round(max(vals), 1))
+        if watts:
+            out.update(median_w=round(statistics.median(watts), 1), min_w=round(min(watts), 1),
+                       max_w=round(max(watts), 1))
         if self.error:
             out["error"] = self.error
         return out
@@ -450,6 +460,15 @@ def bench_default(args, attn, workloads, torch):
         flush_val[0] ^= 1
         scratch.fill_(flush_val[0])
 
+    if args.profile_pass == "long":
+        # the long prefill under sustained load: 30 launches back to back (the counters of
+        # the last ones describe the settled clock)
+        for _ in range(30):
+            long_prefill()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "workload": "long prefill", "launches": 30}))
+        clock.stop()
+        return
     if args.profile_pass:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -648,11 +667,14 @@ def bench_two_legs(args, attn, workloads, torch):
 
                 groups.append((Hg // kv_heads, dec_g, qg.numel()))
                 fns.append(dec_g)
+    clock = ClockSampler().start()
+    clock.mark("settle")
     settle_ms, rounds = settle(fns, args.settle_ms / 1e3)
     for _ in range(args.warmup):
         for f in fns:
             f()
     torch.cuda.synchronize()
+    clock.mark("timed")
     # launches of each kernel before the timed ones (settle rounds and warm-up steps call
     # every function once; a burst starts with one untimed launch)
     before = rounds + args.warmup
@@ -662,7 +684,10 @@ def bench_two_legs(args, attn, workloads, torch):
         dec_ms = flushed_times(dec[0], dec[1], args.steps)
         group_ms = [(G, flushed_times(fn, dec[1], args.steps), nq) for G, fn, nq in groups]
     wall = time.perf_counter() - t0
+    clock.mark("stats")
     pre_stats = burst_stats(prefill, 50, 2 if n > 8192 else 5)
+    clock.mark("idle")
+    clock.stop()
     tf = flops_rate(flops, pre_avg)
     result = {
         "metric": METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -674,7 +699,7 @@ def bench_two_legs(args, attn, workloads, torch):
                    "seq_len": n, "head_dim": d, "causal": True, "window": window},
         "settle": {"ms": round(settle_ms, 1)},
         "prefill": dict({"ms_avg": round(pre_avg, 5), "tflops": round(tf, 2), "flops": flops},
-                        **pre_stats),
+                        **pre_stats, clock=clock.summary({"settle", "timed", "stats"})),
         "roofline": roofline_mfma(tf),
         "trace_index": {"fwd_bf16_kernel": [before + 1, args.steps]},
     }
@@ -1210,7 +1235,8 @@ def main():
                                            "fp8", "cp", "cp-ring", "shapes", "ceilings"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--profile-pass", nargs="?", const="prefill", choices=["prefill", "long"],
+                    default=None)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
