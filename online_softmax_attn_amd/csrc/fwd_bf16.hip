@@ -18,13 +18,14 @@
 //     bf16 weights P^T feed the MFMA B operand straight from the score registers; V^T is
 //     read from a row-major V tile with ds_read_b64_tr_b16, whose 16-lane transpose hands
 //     each lane 4 consecutive keys of one dimension.
-//   * K/V tiles (64 x 128 bf16 = 16 KiB each; 8 KiB at head_dim 64) are double-buffered in LDS and filled by
-//     16-byte-per-lane buffer loads that write LDS directly (no register staging), each lane
-//     fetching the chunk an XOR swizzle puts in its slot; the swizzle keeps both the K row
-//     reads and the transposed V reads free of bank conflicts.  K runs two tiles ahead of
-//     its use, V one.  One barrier per tile.
+//   * K/V tiles (64 x 128 bf16 = 16 KiB each; 8 KiB at head_dim 64) are double-buffered in
+//     LDS and filled by 16-byte-per-lane buffer loads that write LDS directly (no register
+//     staging), each lane fetching the chunk an XOR swizzle puts in its slot; the swizzle
+//     keeps the K row reads and the transposed V reads free of bank conflicts (at head_dim
+//     64 the transposed reads keep a 2-way conflict).  K runs two tiles ahead of its use, V
+//     one.  One barrier per tile.
 //   * the output tile is staged through the then idle K buffers so that every store writes
-//     four whole 256-byte rows.
+//     whole rows (four of 256 bytes; eight of 128 at head_dim 64).
 //   * exp is v_exp_f32 (2^x): scores are scaled by scale*log2(e) inside one FMA.
 //   * the normaliser sums the bf16-ROUNDED weights that enter the P.V product (dot2 with
 //     ones), so rounding of P cancels in u/l to first order.
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int tr_col = 16 * (g & 1) + 4 * (s & 3);           // + 32*db
 
   // ---- building blocks ----------------------------------------------------------------
-  auto compute_s = [&](Tile& T, const bf16* Kt) __attribute__((always_inline)) {  // S^T = K Q^T, 2 kD/16 MFMA + LDS reads
+  auto compute_s = [&](Tile& T, const bf16* Kt) __attribute__((always_inline)) {  // S^T = K Q^T: kD/8 MFMA, as many LDS reads
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
