@@ -1009,7 +1009,8 @@ def bench_ceilings(args, attn, workloads, torch):
     3 back-to-back launches (median): dense matrix-core rate in bf16 and fp8 (blocks of
     ones times blocks of twos, two accumulation chains per wave, two workgroups per CU),
     v_exp_f32 rate (eight chains x <- 2^(-x) per lane), and HBM reads of a 2 GiB buffer,
-    streamed and as 4 KiB pages in a seeded random order (the paged decode's access).
+    streamed and as 4 KiB pages in a seeded random order (the paged decode's access), the
+    latter also after a 1 GiB write per call (the flushed decode's condition).
     Every probe's checksum is verified against the value the work must produce."""
     from online_softmax_attn_amd import binding as b
 
@@ -1077,6 +1078,24 @@ def bench_ceilings(args, attn, workloads, torch):
     line["hbm_pages_4k"] = {"gbs": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
                             "pages": pages, **st}
+    # the same read after a 1 GiB write, as the flushed decode runs: the caches then hold
+    # dirty lines that the reads must evict first
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush_val = [0]
+
+    def flush():
+        flush_val[0] ^= 1
+        scratch.fill_(flush_val[0])
+
+    ms = flushed_times(lambda: b.attn_probe_read_pages(src, order, rb, out=ro), flush, 20)
+    torch.cuda.synchronize()
+    checks["hbm_pages_4k_flushed"] = int(ro.to(torch.int64).sum().item()) % 2**32 == want
+    med = statistics.median(ms)
+    line["hbm_pages_4k_flushed"] = {
+        "gbs": round(nbytes / (med * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+        "frac": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes,
+        **stats(ms, "20 calls, each after a 1 GiB scratch write (median)")}
+    del scratch
     clock.stop()
 
     bf = line["mfma_bf16"]
