@@ -484,7 +484,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int r = (64 / kChunks) * j + lane / kChunks, c = lane % kChunks;
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(stage + r * kD + 8 * (c ^ (r & (kChunks - 1))));
     const int row = m0 + w * 32 + r;
-    if (row < n) *reinterpret_cast<bf16x8*>(O + base + (size_t)row * kD + 8 * c) = y;
+    // written once and never read here: streamed past the caches, which keep K and V (as
+    // whole rows; lane-scattered pieces stored this way would each go to memory alone)
+    if (row < n) __builtin_nontemporal_store(y, reinterpret_cast<bf16x8*>(O + base + (size_t)row * kD + 8 * c));
   }
   if (LSE && hl == 0 && qi - q_start < n)
     LSE[(size_t)bh * n + (qi - q_start)] = valid ? (m_ref * ATTN_LN2 + __logf(l_tot)) : -INFINITY;

@@ -339,23 +339,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   asm volatile("s_mov_b32 %0, 0" : "=s"(hidden_zero));
   sweep(tiles[0] + hidden_zero, tiles[1] + hidden_zero, tiles[2] + hidden_zero, tiles[3] + hidden_zero);
 
-  // ---- epilogue: o = u / l (l is the whole row's sum: every lane of the MFMA column has it)
-  if (qi < n) {
-    bf16* orow = O + o_base + (size_t)qi * kD;
-    const bool valid = qi < L;
-    const float inv = 1.0f / l_acc;
+  // ---- epilogue: o = u / l (l is the whole row's sum: every lane of the MFMA column has it),
+  // staged through LDS so that each store writes four whole 256-byte rows of O: once every
+  // wave is past its last tile the four slots (32 KiB) are free, and wave w takes 32 rows,
+  // the 16-byte chunks of row r XOR-swizzled by r % 16.
+  __syncthreads();
+  const bool valid = qi < L;
+  const float inv = 1.0f / l_acc;
+  bf16* stage = reinterpret_cast<bf16*>(&tiles[0][0]) + w * (32 * kD);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        floatx4 x;
+    for (int a = 0; a < 4; ++a) {
+      floatx4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = valid ? acc[db][4 * a + e] * inv : 0.f;
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * a + 4 * hl) = __builtin_convertvector(x, bf16x4);
-      }
-    if (LSE && hl == 0)
-      LSE[(size_t)bh * n + qi] = valid ? (m_ref * ATTN_LN2 + __logf(l_acc)) : -INFINITY;
+      for (int e = 0; e < 4; ++e) x[e] = valid ? acc[db][4 * a + e] * inv : 0.f;
+      const int chunk = (4 * db + a) ^ (lq & 15);
+      *reinterpret_cast<bf16x4*>(stage + lq * kD + 8 * chunk + 4 * hl) = __builtin_convertvector(x, bf16x4);
+    }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 4 * j + lane / 16, c = lane % 16;
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(stage + r * kD + 8 * (c ^ (r & 15)));
+    const int row = m0 + 32 * w + r;
+    // written once and never read here: streamed past the caches, which keep K and V
+    if (row < n) __builtin_nontemporal_store(y, reinterpret_cast<bf16x8*>(O + o_base + (size_t)row * kD + 8 * c));
   }
+  if (LSE && hl == 0 && qi < n)
+    LSE[(size_t)bh * n + qi] = valid ? (m_ref * ATTN_LN2 + __logf(l_acc)) : -INFINITY;
 }
 
 }  // namespace
