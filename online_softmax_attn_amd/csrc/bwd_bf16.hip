@@ -253,11 +253,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   asm volatile("s_mov_b32 %0, 0" : "=s"(hidden_zero));
   sweep(tiles[0] + hidden_zero, tiles[1] + hidden_zero, tiles[2] + hidden_zero, tiles[3] + hidden_zero);
 
-  if (qi < n) {
-    // the lane's half index is taken afresh from the lane id (mbcnt) rather than kept live
-    // through the key loop, which runs at the register limit
-    const int hl_out = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
-    float* drow = dQ + base + (size_t)qi * kD + 4 * hl_out;
+  // dQ rows staged through LDS so that each store writes two whole 512-byte rows: every wave
+  // is past the last step's barrier, so the four slots (64 KiB) are free and wave w takes
+  // slot w for its 32 rows, the 16-byte chunks of row r XOR-swizzled by r.  The lane's
+  // indices are taken afresh from the lane id (mbcnt) rather than kept live through the key
+  // loop, which runs at the register limit.
+  {
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int hl_out = ln >> 5, lq_out = ln & 31;
+    const int row0 = __builtin_amdgcn_readfirstlane(qi - lq_out);  // m0 + 32 w
+    floatx4* stage = reinterpret_cast<floatx4*>(tiles[(row0 - m0) >> 5]);  // 32 rows x 32 chunks
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -265,8 +270,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         floatx4 x;
 #pragma unroll
         for (int c = 0; c < 4; ++c) x[c] = row_ok ? acc[db][4 * a + c] * scale : 0.f;
-        *reinterpret_cast<floatx4*>(drow + 32 * db + 8 * a) = x;
+        // d = 32 db + 8 a + 4 hl .. +3 is chunk 8 db + 2 a + hl of the row
+        stage[32 * lq_out + ((8 * db + 2 * a + hl_out) ^ lq_out)] = x;
       }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 2 * j + hl_out, c = lq_out;
+      const int row = row0 + r;
+      // written once and never read here: streamed past the caches
+      if (row < n) __builtin_nontemporal_store(stage[32 * r + (c ^ r)], reinterpret_cast<floatx4*>(dQ + base + (size_t)row * kD + 4 * c));
+    }
   }
 }
 
@@ -545,18 +559,35 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dkdv_kernel(
            Ds[0] + hidden_zero, Ds[1] + hidden_zero, &Ps[0][0][0][0] + hidden_zero);
   }
 
-  if (kj < n) {
-    float* row = (vwave ? dV : dK) + kv_base + (size_t)kj * kD;
-    const float f = vwave ? 1.f : scale;
+  // dV (V-waves) then dK (K-waves), staged through LDS so that each store writes two whole
+  // 512-byte rows: every wave is past the last step's barrier, so the Q and dO slots (64
+  // KiB) are free; the four waves of a group take 16 KiB each (32 rows, the 16-byte chunks
+  // of row r XOR-swizzled by r), one group after the other.
+  floatx4* stage = reinterpret_cast<floatx4*>(&lds) + pair * (32 * 32);
+  const float f = vwave ? 1.f : scale;
+  float* out = vwave ? dV : dK;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int phase = 0; phase < 2; ++phase) {
+    if (phase == 1) __syncthreads();  // the V-waves have read their rows back
+    if (vwave == (phase == 0)) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        floatx4 x;
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) x[c] = key_ok ? acc[db][4 * a + c] * f : 0.f;
-        *reinterpret_cast<floatx4*>(row + 32 * db + 8 * a + 4 * hl) = x;
+        for (int a = 0; a < 4; ++a) {
+          floatx4 x;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) x[c] = key_ok ? acc[db][4 * a + c] * f : 0.f;
+          stage[32 * lq + ((8 * db + 2 * a + hl) ^ lq)] = x;
+        }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = 2 * j + hl, c = lq;
+        const int row = k0 + 32 * pair + r;
+        // written once and never read here: streamed past the caches
+        if (row < n) __builtin_nontemporal_store(stage[32 * r + (c ^ r)], reinterpret_cast<floatx4*>(out + kv_base + (size_t)row * kD + 4 * c));
       }
+    }
   }
 }
 
