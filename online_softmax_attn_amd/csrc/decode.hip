@@ -231,11 +231,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         lo[c] = a[c];
         hi[c] = a[4 + c];
       }
-      *reinterpret_cast<floatx4*>(u) = lo;
-      *reinterpret_cast<floatx4*>(u + 4) = hi;
+      // streamed past the caches (the sixteen lanes write the head's whole 512-byte row):
+      // 1.2% faster on the decode workload with a cache flush before each call
+      __builtin_nontemporal_store(lo, reinterpret_cast<floatx4*>(u));
+      __builtin_nontemporal_store(hi, reinterpret_cast<floatx4*>(u + 4));
       if (lane == 0) {
-        P.m[p] = m_run[g];
-        P.l[p] = l_tot;
+        __builtin_nontemporal_store(m_run[g], P.m + p);
+        __builtin_nontemporal_store(l_tot, P.l + p);
       }
     }
   }
