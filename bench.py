@@ -403,12 +403,23 @@ def parity(prefill_o, prefill_ref, pw, decode_o, lw, long_o):
     got = np.stack([prefill_o[b, h] for b, h in keys])
     want = np.stack([prefill_ref[k] for k in keys])
     out["prefill"] = dict(parity_entry(got, want), heads=len(keys))
+    # the oracle's own time on each reference it computes here (algorithmic flops: 4 d per
+    # admitted (query, key) pair), beside the prefill's in cpu_baseline
+    t0 = time.perf_counter()
     ro, _ = oracle.decode(pw.q, pw.k_seqs, pw.v_seqs)
-    out["decode"] = parity_entry(decode_o, ro)
+    dt = time.perf_counter() - t0
+    H, d = pw.q.shape[1], pw.q.shape[2]
+    fl = 4 * d * H * sum(int(x.shape[1]) for x in pw.k_seqs)
+    out["decode"] = dict(parity_entry(decode_o, ro), oracle_s=round(dt, 3),
+                         oracle_gflops=round(fl / dt / 1e9, 3))
     rows = lw["rows"].numpy()
+    t0 = time.perf_counter()
     ro, _ = oracle.attention_rows(lw["q"], lw["k"], lw["v"], rows, causal=True)
+    dt = time.perf_counter() - t0
+    fl = 4 * lw["q"].shape[-1] * int((rows + 1).sum())
     got = np.stack([long_o[0, h, rows[h]] for h in range(rows.shape[0])])[None]
-    out["long_prefill"] = dict(parity_entry(got, ro), rows=f"{rows.shape[1]} seeded rows per head")
+    out["long_prefill"] = dict(parity_entry(got, ro), rows=f"{rows.shape[1]} seeded rows per head",
+                               oracle_s=round(dt, 3), oracle_gflops=round(fl / dt / 1e9, 3))
     return out
 
 
