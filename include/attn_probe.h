@@ -15,7 +15,7 @@
  *
  * Conventions: as include/attn.h (device pointers owned by the caller, work enqueued on
  * `stream`, nothing allocated, host-visible arguments checked first, ATTN_ERR_INVALID for a
- * null pointer or a size <= 0).  Each kernel writes a checksum the caller can verify, so
+ * null pointer, a size <= 0 or more than 2^24 workgroups).  Each kernel writes a checksum the caller can verify, so
  * the work cannot be elided:
  *   - the matrix-core probes multiply blocks of ones by blocks of twos: every accumulator
  *     element ends at 32 * iters (bf16) or 128 * iters (fp8), and `out[w]` for each wave w

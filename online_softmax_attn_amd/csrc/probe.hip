@@ -123,12 +123,15 @@ __global__ __launch_bounds__(kThreads) void probe_read_pages_kernel(
 
 attn_status launched() { return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
+constexpr int kMaxBlocks = 1 << 24;  // keeps every output index within 32 bits
+bool bad_blocks(int blocks) { return blocks <= 0 || blocks > kMaxBlocks; }
+
 }  // namespace
 
 extern "C" {
 
 attn_status attn_probe_mfma(int fp8, int blocks, int iters, float* out, void* stream) {
-  if (!out || blocks <= 0 || iters <= 0 || iters > 16384 || (fp8 != 0 && fp8 != 1))
+  if (!out || bad_blocks(blocks) || iters <= 0 || iters > 16384 || (fp8 != 0 && fp8 != 1))
     return ATTN_ERR_INVALID;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (fp8)
@@ -139,7 +142,7 @@ attn_status attn_probe_mfma(int fp8, int blocks, int iters, float* out, void* st
 }
 
 attn_status attn_probe_exp(int blocks, int iters, float* out, void* stream) {
-  if (!out || blocks <= 0 || iters <= 0) return ATTN_ERR_INVALID;
+  if (!out || bad_blocks(blocks) || iters <= 0) return ATTN_ERR_INVALID;
   hipLaunchKernelGGL(probe_exp_kernel, dim3(blocks), dim3(kThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), iters, out);
   return launched();
@@ -147,7 +150,7 @@ attn_status attn_probe_exp(int blocks, int iters, float* out, void* stream) {
 
 attn_status attn_probe_read(const void* src, size_t bytes, int blocks, uint32_t* out,
                             void* stream) {
-  if (!src || !out || bytes == 0 || bytes % 4096 != 0 || blocks <= 0) return ATTN_ERR_INVALID;
+  if (!src || !out || bytes == 0 || bytes % 4096 != 0 || bad_blocks(blocks)) return ATTN_ERR_INVALID;
   hipLaunchKernelGGL(probe_read_kernel, dim3(blocks), dim3(kThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
                      bytes / 16, out);
@@ -156,7 +159,7 @@ attn_status attn_probe_read(const void* src, size_t bytes, int blocks, uint32_t*
 
 attn_status attn_probe_read_pages(const void* pool, int pool_pages, const int32_t* order,
                                   int n_pages, int blocks, uint32_t* out, void* stream) {
-  if (!pool || !order || !out || pool_pages <= 0 || n_pages <= 0 || blocks <= 0)
+  if (!pool || !order || !out || pool_pages <= 0 || n_pages <= 0 || bad_blocks(blocks))
     return ATTN_ERR_INVALID;
   hipLaunchKernelGGL(probe_read_pages_kernel, dim3(blocks), dim3(kThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(pool),

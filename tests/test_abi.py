@@ -61,6 +61,10 @@ def test_library_exports_every_probe_function():
     lambda L: L.attn_probe_read_pages(FAKE, 0, FAKE, 8, 1, FAKE, None),
     lambda L: L.attn_probe_read_pages(FAKE, 8, FAKE, 0, 1, FAKE, None),
     lambda L: L.attn_probe_read_pages(None, 8, FAKE, 8, 1, FAKE, None),
+    lambda L: L.attn_probe_mfma(0, (1 << 24) + 1, 1, FAKE, None),
+    lambda L: L.attn_probe_exp((1 << 24) + 1, 1, FAKE, None),
+    lambda L: L.attn_probe_read(FAKE, 4096, (1 << 24) + 1, FAKE, None),
+    lambda L: L.attn_probe_read_pages(FAKE, 8, FAKE, 8, (1 << 24) + 1, FAKE, None),
 ])
 def test_probe_validation(call):
     assert call(attn.lib()) == INVALID
